@@ -1,0 +1,486 @@
+"""Pins of the CPU oracle to things other than itself: page-printed values,
+closed forms, invariants, brute force on tiny inputs and library routines.
+
+Each test names the oracle function it pins and what a plausible mistake
+(dropped term, wrong sign or index, transposed operand) would do to it."""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import qv_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden_rows(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as fh:
+        for line in fh:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                rows.append(line)
+    return rows
+
+
+# ------------------------------------------------------------------ grid
+def test_grid_page_values():
+    """smart_resize / grid_thw against the grid and token counts the pages print."""
+    for row in _golden_rows("page_grids.txt"):
+        lhs, rhs = row.split("->")
+        h, w, f = map(int, lhs.split())
+        t, gh, gw, n, m = map(int, rhs.split())
+        hh, ww, g = O.grid_thw(h, w, f)
+        assert (hh, ww) == (h, w)
+        assert g == (t, gh, gw)
+        assert t * gh * gw == n
+        assert hh * ww // 784 == m == n // 4
+
+
+def _nearest_multiple_even_tie(x, f):
+    """Brute force: the multiple of f nearest to x (ties to the even multiple), >= f."""
+    best = None
+    for k in range(1, x // f + 3):
+        d = abs(k * f - x)
+        key = (d, k % 2)  # equal distance: prefer even k
+        if best is None or key < best[0]:
+            best = (key, k * f)
+    return best[1]
+
+
+def test_grid_bruteforce_properties():
+    """Every result: sides multiples of 28, tokens in [4, 16384]; in-budget sides
+    equal the brute-force nearest multiple; over/under budget sides are the
+    largest/smallest multiples of the common rescale."""
+    f = 28
+    rng = np.random.default_rng(123)
+    cases = [(h, w) for h in range(1, 2001, 13) for w in range(1, 2001, 17)]
+    cases += [tuple(x) for x in rng.integers(1, 6000, size=(3000, 2))]
+    for h, w in cases:
+        try:
+            hh, ww = O.smart_resize(int(h), int(w))
+        except ValueError:
+            # only extreme aspect ratios may fail
+            assert max(h, w) / min(h, w) > 100
+            continue
+        assert hh % f == 0 and ww % f == 0
+        assert 4 <= hh * ww // 784 <= 16384
+        nh, nw = _nearest_multiple_even_tie(int(h), f), _nearest_multiple_even_tie(int(w), f)
+        if O.MIN_PIXELS <= nh * nw <= O.MAX_PIXELS:
+            assert (hh, ww) == (nh, nw)
+        elif nh * nw > O.MAX_PIXELS:
+            s = math.sqrt(O.MAX_PIXELS / (h * w))
+            assert hh <= max(f, h * s + 1e-9) and (hh == f or hh + f > h * s - 1e-9)
+        else:
+            s = math.sqrt(O.MIN_PIXELS / (h * w))
+            assert hh >= h * s - 1e-9 and hh - f < h * s + 1e-9
+
+
+def test_grid_idempotent_and_token_formula():
+    """Valid sides map to themselves and tokens = pixels / 784 (Qwen2.5-VL record)."""
+    for h in range(56, 3585, 28 * 7):
+        for w in range(56, 3585, 28 * 5):
+            if not (O.MIN_PIXELS <= h * w <= O.MAX_PIXELS):
+                continue
+            hh, ww, g = O.grid_thw(h, w)
+            assert (hh, ww) == (h, w)
+            assert g[1] * g[2] // 4 == h * w // 784
+    # the round-half-even tie: 70 = 2.5 * 28 goes to 56, 98 = 3.5 * 28 to 112
+    assert O.smart_resize(70, 112)[0] == 56
+    assert O.smart_resize(98, 112)[0] == 112
+
+
+def test_grid_frames():
+    assert O.grid_thw(56, 56, 1)[2][0] == 1
+    assert O.grid_thw(56, 56, 2)[2][0] == 1
+    assert O.grid_thw(56, 56, 3)[2][0] == 2
+
+
+# ------------------------------------------------------- order / positions
+def test_merge_order_golden_4x4():
+    cu, pos, perm = O.seq_meta([(1, 4, 4)])
+    want = np.array([list(map(int, r.split())) for r in _golden_rows("merge_order_4x4.txt")])
+    assert (perm == want[:, 1]).all()
+    assert (pos == want[:, 2:4]).all()
+    assert list(cu) == [0, 16]
+
+
+def test_seq_meta_bijection_and_cu():
+    grids = [(1, 4, 6), (2, 2, 2), (1, 48, 48), (1, 6, 10)]
+    cu, pos, perm = O.seq_meta(grids)
+    assert list(cu) == [0, 24, 32, 32 + 2304, 32 + 2304 + 60]
+    for i, (t, gh, gw) in enumerate(grids):
+        p = perm[cu[i]:cu[i + 1]]
+        assert sorted(p.tolist()) == list(range(t * gh * gw))
+        # (h, w) agrees with the raster index
+        assert (pos[cu[i]:cu[i + 1], 0] == (p % (gh * gw)) // gw).all()
+        assert (pos[cu[i]:cu[i + 1], 1] == p % gw).all()
+    # four 672x672 images: cu_seqlens 0, 2304, ..., 9216 (packed-batch workload)
+    cu4, _, _ = O.seq_meta([(1, 48, 48)] * 4)
+    assert list(cu4) == [0, 2304, 4608, 6912, 9216]
+    with pytest.raises(ValueError):
+        O.seq_meta([(1, 3, 4)])
+
+
+def test_strided_slice_identity():
+    """LiteRT-LM card: raster order + four strided slices concatenated equals the
+    merge-group order reshaped to [N/4][4C]."""
+    rng = np.random.default_rng(0)
+    for gh, gw in [(4, 4), (6, 10), (8, 2)]:
+        c = 5
+        f = rng.standard_normal((gh, gw, c))
+        slices = [f[0::2, 0::2], f[0::2, 1::2], f[1::2, 0::2], f[1::2, 1::2]]
+        ref = np.concatenate(slices, axis=-1).reshape(-1, 4 * c)
+        _, _, perm = O.seq_meta([(1, gh, gw)])
+        got = f.reshape(gh * gw, c)[perm].reshape(-1, 4 * c)
+        assert np.array_equal(ref, got)
+
+
+# --------------------------------------------------- patchify / patch-embed
+def _conv3d_reference(frames, weight):
+    """torch conv3d (CPU, float64) on frames padded to a multiple of 2."""
+    fr = frames
+    if fr.shape[0] % 2:
+        fr = np.concatenate([fr, fr[-1:]], axis=0)
+    x = torch.from_numpy(fr.astype(np.float64)).permute(1, 0, 2, 3)[None]  # [1][C][F][H][W]
+    y = F.conv3d(x, torch.from_numpy(weight.astype(np.float64)), stride=(2, 14, 14))
+    return y[0].permute(1, 2, 3, 0).reshape(-1, weight.shape[0]).numpy()  # raster [T*gh*gw][out]
+
+
+def test_patch_embed_equals_conv3d():
+    rng = np.random.default_rng(1)
+    out = 16
+    w = rng.standard_normal((out, 3, 2, 14, 14))
+    for (h, wd, f) in [(56, 84, 1), (28, 112, 2), (84, 56, 3)]:
+        img = rng.uniform(-1, 1, (f, 3, h, wd)).astype(np.float32)
+        g = O.grid_thw(h, wd, f)[2]
+        x = O.patchify([img], [g])
+        got = O.patch_embed(x.astype(np.float64), w)
+        _, _, perm = O.seq_meta([g])
+        ref = _conv3d_reference(img, w)[perm]
+        np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_conv2d_fold_for_still_image():
+    """LiteRT-LM card: Conv3d over the duplicated still frame equals Conv2d with
+    the summed temporal kernel w[:,:,0] + w[:,:,1]."""
+    rng = np.random.default_rng(2)
+    w = rng.standard_normal((8, 3, 2, 14, 14))
+    img = rng.uniform(-1, 1, (1, 3, 56, 84)).astype(np.float32)
+    g = O.grid_thw(56, 84, 1)[2]
+    got = O.patch_embed(O.patchify([img], [g]).astype(np.float64), w)
+    x2 = torch.from_numpy(img[0].astype(np.float64))[None]
+    y = F.conv2d(x2, torch.from_numpy(w[:, :, 0] + w[:, :, 1]), stride=14)[0]
+    ref = y.permute(1, 2, 0).reshape(-1, 8).numpy()
+    _, _, perm = O.seq_meta([g])
+    np.testing.assert_allclose(got, ref[perm], rtol=1e-12, atol=1e-12)
+
+
+def test_patchify_rejects_off_grid():
+    img = np.zeros((1, 3, 56, 57), np.float32)
+    with pytest.raises(ValueError):
+        O.raster_patches(img, (1, 4, 4))
+
+
+# ----------------------------------------------------------------- bf16 cast
+def test_bf16_round_matches_torch():
+    rng = np.random.default_rng(3)
+    x = np.concatenate([rng.standard_normal(20000).astype(np.float32) * 10.0 ** rng.integers(-8, 8, 20000),
+                        np.array([0.0, -0.0, 1.0, 1.00390625, 1.01171875, 3.0e38, -1e-40], np.float32)])
+    x = x.astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.bf16_round(x), ref)
+    assert np.array_equal(O.bf16_to_float(O.bf16_round(x)), torch.from_numpy(x).to(torch.bfloat16).float().numpy())
+
+
+# ---------------------------------------------------------------------- rope
+def _rand_heads(rng, n, heads=2, hd=80):
+    return rng.standard_normal((n, heads, hd))
+
+
+def test_rope_closed_form_angles():
+    """omega_k = 1e4^(-k/20): omega_5 = 0.1, omega_10 = 0.01, omega_15 = 0.001; pairs
+    0..19 turn with h, 20..39 with w; pair j couples elements j and j+40."""
+    pos = np.array([[3, 0], [0, 7], [1, 0]])
+    a = O.rope_angles(pos)
+    assert a[0, 5] == pytest.approx(0.3, rel=1e-14)
+    assert a[0, 10] == pytest.approx(0.03, rel=1e-14)
+    assert a[1, 20 + 15] == pytest.approx(0.007, rel=1e-13)
+    assert (a[0, 20:] == 0).all() and (a[1, :20] == 0).all()
+    x = np.zeros((3, 1, 80))
+    x[:, 0, 5] = 1.0
+    y = O.apply_rope(x, a)
+    assert y[0, 0, 5] == pytest.approx(math.cos(0.3)) and y[0, 0, 45] == pytest.approx(math.sin(0.3))
+    assert y[1, 0, 5] == 1.0 and y[1, 0, 45] == 0.0    # w rotation leaves pair 5 alone
+    x2 = np.zeros((3, 1, 80))
+    x2[:, 0, 40] = 1.0                                   # second element of pair 0
+    y2 = O.apply_rope(x2, a)
+    assert y2[2, 0, 0] == pytest.approx(-math.sin(1.0)) and y2[2, 0, 40] == pytest.approx(math.cos(1.0))
+
+
+def test_rope_norm_and_identity():
+    rng = np.random.default_rng(4)
+    x = _rand_heads(rng, 50)
+    pos = rng.integers(0, 256, size=(50, 2))
+    y = O.apply_rope(x, O.rope_angles(pos))
+    np.testing.assert_allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-12)
+    z = O.apply_rope(x, O.rope_angles(np.zeros((50, 2), np.int64)))
+    np.testing.assert_array_equal(z, x)
+
+
+def test_rope_relative_offset():
+    """(R_p q) . (R_r k) depends only on p - r."""
+    rng = np.random.default_rng(5)
+    q = _rand_heads(rng, 1, 1)
+    k = _rand_heads(rng, 1, 1)
+    for _ in range(20):
+        p, r, s = rng.integers(0, 200, size=(3, 2))
+        lhs = (O.apply_rope(q, O.rope_angles(p[None])) * O.apply_rope(k, O.rope_angles(r[None]))).sum()
+        rhs = (O.apply_rope(q, O.rope_angles((p + s)[None])) * O.apply_rope(k, O.rope_angles((r + s)[None]))).sum()
+        assert lhs == pytest.approx(rhs, rel=1e-9, abs=1e-9)
+        d = (O.apply_rope(q, O.rope_angles((p - r)[None])) * k).sum()
+        assert lhs == pytest.approx(d, rel=1e-9, abs=1e-9)
+
+
+# ------------------------------------------------------------- layer norm
+def test_layer_norm_vs_torch_and_moments():
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((33, 1280)) * 3 + 1.5
+    g = 1 + 0.02 * rng.standard_normal(1280)
+    b = 0.02 * rng.standard_normal(1280)
+    ref = F.layer_norm(torch.from_numpy(x), (1280,), torch.from_numpy(g), torch.from_numpy(b), eps=1e-6).numpy()
+    np.testing.assert_allclose(O.layer_norm(x, g, b, 1e-6), ref, rtol=1e-12, atol=1e-12)
+    y = O.layer_norm(x, np.ones(1280), np.zeros(1280), 1e-6)
+    np.testing.assert_allclose(y.mean(axis=1), 0, atol=1e-12)
+    np.testing.assert_allclose(y.var(axis=1), 1, rtol=1e-5)
+
+
+# ----------------------------------------------------------- activations
+def test_gelu_and_quick_gelu():
+    u = np.linspace(-9, 9, 1001)
+    np.testing.assert_allclose(O.gelu_erf(u), F.gelu(torch.from_numpy(u), approximate="none").numpy(),
+                               rtol=1e-12, atol=1e-14)
+    # g(u) - g(-u) = u for both (sigmoid(x) + sigmoid(-x) = 1, erf odd)
+    np.testing.assert_allclose(O.quick_gelu(u) - O.quick_gelu(-u), u, atol=1e-12)
+    np.testing.assert_allclose(O.gelu_erf(u) - O.gelu_erf(-u), u, atol=1e-12)
+    assert O.quick_gelu(np.array([0.0]))[0] == 0.0
+    # slope 1/2 at the origin, and the 1.702 factor: d/du at 0 of u*sig(a u) = 1/2; second
+    # derivative at 0 is a/2
+    e = 1e-4
+    second = (O.quick_gelu(np.array([e]))[0] + O.quick_gelu(np.array([-e]))[0]) / e ** 2
+    assert second == pytest.approx(1.702 / 2, rel=1e-4)
+
+
+# --------------------------------------------------------------- attention
+def _brute_attention(q, k, v, cu):
+    n, heads, hd = q.shape
+    out = np.zeros_like(q)
+    for i in range(len(cu) - 1):
+        for h in range(heads):
+            for a in range(cu[i], cu[i + 1]):
+                s = [sum(q[a, h, d] * k[b, h, d] for d in range(hd)) / math.sqrt(hd)
+                     for b in range(cu[i], cu[i + 1])]
+                m = max(s)
+                e = [math.exp(x - m) for x in s]
+                z = sum(e)
+                for d in range(hd):
+                    out[a, h, d] = sum(e[j] * v[cu[i] + j, h, d] for j in range(len(e))) / z
+    return out
+
+
+def test_attention_bruteforce_tiny():
+    rng = np.random.default_rng(7)
+    cu = np.array([0, 4, 12, 16])
+    q, k, v = (rng.standard_normal((16, 2, 6)) for _ in range(3))
+    np.testing.assert_allclose(O.attention_varlen(q, k, v, cu), _brute_attention(q, k, v, cu), rtol=1e-12,
+                               atol=1e-12)
+
+
+def test_attention_vs_sdpa_block_diagonal_and_packed():
+    rng = np.random.default_rng(8)
+    cu = np.array([0, 24, 40, 100])
+    n = 100
+    q, k, v = (rng.standard_normal((n, 3, 80)) for _ in range(3))
+    seg = np.searchsorted(cu, np.arange(n), side="right") - 1
+    mask = torch.from_numpy(seg[:, None] == seg[None, :])
+    t = lambda a: torch.from_numpy(a).permute(1, 0, 2)
+    ref = F.scaled_dot_product_attention(t(q), t(k), t(v), attn_mask=mask).permute(1, 0, 2).numpy()
+    got = O.attention_varlen(q, k, v, cu)
+    np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-12)
+    # packed == per image
+    for i in range(3):
+        a, b = cu[i], cu[i + 1]
+        one = O.attention_varlen(q[a:b], k[a:b], v[a:b], np.array([0, b - a]))
+        np.testing.assert_allclose(got[a:b], one, rtol=1e-12, atol=1e-12)
+    # restricted query rows give the same rows
+    rows = np.array([3, 30, 99, 41])
+    np.testing.assert_allclose(O.attention_varlen(q, k, v, cu, q_rows=rows), got[rows], rtol=1e-12)
+
+
+def test_attention_equal_keys_is_mean_of_values():
+    rng = np.random.default_rng(9)
+    q = rng.standard_normal((8, 1, 80))
+    k = np.repeat(rng.standard_normal((1, 1, 80)), 8, axis=0)
+    v = rng.standard_normal((8, 1, 80))
+    got = O.attention_varlen(q, k, v, np.array([0, 8]))
+    np.testing.assert_allclose(got, np.repeat(v.mean(axis=0, keepdims=True), 8, axis=0), rtol=1e-12)
+
+
+def test_attention_position_shift_invariance():
+    """Adding one constant (dh, dw) to every position leaves rotary attention unchanged."""
+    rng = np.random.default_rng(10)
+    cu, pos, _ = O.seq_meta([(1, 4, 6)])
+    q, k, v = (rng.standard_normal((24, 2, 80)) for _ in range(3))
+    out = []
+    for shift in ([0, 0], [5, 11]):
+        a = O.rope_angles(pos + np.array(shift))
+        out.append(O.attention_varlen(O.apply_rope(q, a), O.apply_rope(k, a), v, cu))
+    np.testing.assert_allclose(out[0], out[1], rtol=1e-9, atol=1e-12)
+
+
+# --------------------------------------------------------------- the block
+def _block_params(rng, d=1280, m=5120, scale=0.02):
+    p = {"ln1_w": 1 + scale * rng.standard_normal(d), "ln1_b": scale * rng.standard_normal(d),
+         "qkv_w": scale * rng.standard_normal((3 * d, d)), "qkv_b": scale * rng.standard_normal(3 * d),
+         "proj_w": scale * rng.standard_normal((d, d)), "proj_b": scale * rng.standard_normal(d),
+         "ln2_w": 1 + scale * rng.standard_normal(d), "ln2_b": scale * rng.standard_normal(d),
+         "fc1_w": scale * rng.standard_normal((m, d)), "fc1_b": scale * rng.standard_normal(m),
+         "fc2_w": scale * rng.standard_normal((d, m)), "fc2_b": scale * rng.standard_normal(d)}
+    return p
+
+
+def test_block_uniform_attention_special_case():
+    """With the q and k thirds of W_qkv and b_qkv zero, every score is 0, so each
+    token attends uniformly to its own image: o = image mean of the value rows.
+    With W_fc2 = 0 the MLP adds b2.  Pins the [q|k|v] split, value rows not
+    rotated, per-image segments, and both residual adds of a pre-norm block."""
+    rng = np.random.default_rng(11)
+    d = 1280
+    p = _block_params(rng)
+    p["qkv_w"][:2 * d] = 0
+    p["qkv_b"][:2 * d] = 0
+    p["fc2_w"][:] = 0
+    grids = [(1, 2, 4), (1, 4, 4)]
+    cu, pos, _ = O.seq_meta(grids)
+    z = rng.standard_normal((cu[-1], d))
+    got = O.vision_block(z, p, cu, O.rope_angles(pos))
+    a = (z - z.mean(1, keepdims=True)) / np.sqrt(z.var(1, keepdims=True) + 1e-6) * p["ln1_w"] + p["ln1_b"]
+    vrows = a @ p["qkv_w"][2 * d:].T + p["qkv_b"][2 * d:]
+    want = np.empty_like(z)
+    for i in range(len(grids)):
+        s = slice(cu[i], cu[i + 1])
+        want[s] = z[s] + vrows[s].mean(axis=0) @ p["proj_w"].T + p["proj_b"] + p["fc2_b"]
+    np.testing.assert_allclose(got, want, rtol=1e-10, atol=1e-10)
+
+
+def test_block_is_pre_norm_scale_invariant():
+    """Pre-norm: each half adds f(LN(input)) to its input.  With the MLP's output
+    weight zero (so it adds only b2), block(c z) - c z equals block(z) - z for
+    c > 0 (up to eps); likewise with the attention projection zeroed.  A
+    post-norm block (LN after the residual add) fails both."""
+    rng = np.random.default_rng(12)
+    cu, pos, _ = O.seq_meta([(1, 4, 4)])
+    z = rng.standard_normal((16, 1280))
+    a = O.rope_angles(pos)
+    for zero in (("fc2_w",), ("proj_w", "proj_b")):
+        p = _block_params(rng)
+        for key in zero:
+            p[key][:] = 0
+        d1 = O.vision_block(z, p, cu, a) - z
+        d2 = O.vision_block(7.0 * z, p, cu, a) - 7.0 * z
+        np.testing.assert_allclose(d1, d2, rtol=1e-5, atol=1e-5)
+
+
+def test_block_rows_equals_block():
+    rng = np.random.default_rng(13)
+    p = _block_params(rng)
+    grids = [(1, 4, 4), (1, 6, 2), (1, 2, 2)]
+    cu, pos, _ = O.seq_meta(grids)
+    z = rng.standard_normal((cu[-1], 1280))
+    a = O.rope_angles(pos)
+    full = O.vision_block(z, p, cu, a)
+    rows = np.array([0, 5, 17, 20, 27, 31])
+    np.testing.assert_allclose(O.vision_block_rows(z, p, cu, a, rows), full[rows], rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------- merger
+def test_merger_identity_special_case_and_shapes():
+    """fc1 = I, b1 = 0, fc2 = I[:out], b2 = 0 leaves GELU(LN(z) grouped) — pins
+    LN before grouping, the 4-token concat, GELU-erf between the Linears."""
+    rng = np.random.default_rng(14)
+    d, n = 8, 12
+    z = rng.standard_normal((n, d))
+    p = {"merger.ln_w": 1 + 0.1 * rng.standard_normal(d), "merger.ln_b": 0.1 * rng.standard_normal(d),
+         "merger.fc1_w": np.eye(4 * d), "merger.fc1_b": np.zeros(4 * d),
+         "merger.fc2_w": np.eye(4 * d)[:5], "merger.fc2_b": np.zeros(5)}
+    got = O.patch_merge(z, p)
+    ln = F.layer_norm(torch.from_numpy(z), (d,), torch.from_numpy(p["merger.ln_w"]),
+                      torch.from_numpy(p["merger.ln_b"]), eps=1e-6)
+    ref = F.gelu(ln.reshape(n // 4, 4 * d))[:, :5].numpy()
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+    with pytest.raises(ValueError):
+        O.patch_merge(z[:10], p)
+
+
+def test_page_shapes_through_merger():
+    """Encoder/adapter shapes of the pages: rows N and N/4, widths 1280 and out_dim."""
+    for row in _golden_rows("page_shapes.txt"):
+        lhs, rhs = row.split("->")
+        h, w, out_dim = map(int, lhs.split())
+        n, dw, m, mw = map(int, rhs.split())
+        g = O.grid_thw(h, w)[2]
+        cu, _, _ = O.seq_meta([g])
+        assert cu[-1] == n and dw == 1280
+        z = np.zeros((n, 16))
+        p = {"merger.ln_w": np.ones(16), "merger.ln_b": np.zeros(16), "merger.fc1_w": np.zeros((64, 64)),
+             "merger.fc1_b": np.zeros(64), "merger.fc2_w": np.zeros((out_dim, 64)),
+             "merger.fc2_b": np.zeros(out_dim)}
+        assert O.patch_merge(z, p).shape == (m, mw)
+
+
+# -------------------------------------------------------------- the tower
+def test_tower_raster_order_equals_block_order():
+    """LiteRT-LM card: running the blocks in raster order, each patch carrying its
+    own 2-D rope, then merging by four strided slices equals the block-order
+    encoder followed by the contiguous merge."""
+    rng = np.random.default_rng(15)
+    d = 1280
+    grids = [(1, 4, 6), (1, 4, 4)]
+    imgs = [rng.uniform(-1, 1, (1, 3, 14 * g[1], 14 * g[2])).astype(np.float32) for g in grids]
+    params = {"patch_w": 0.02 * rng.standard_normal((d, 3, 2, 14, 14))}
+    for k, v in _block_params(rng).items():
+        params["blocks.0." + k] = v
+    for k, v in {"ln_w": 1 + 0.02 * rng.standard_normal(d), "ln_b": 0.02 * rng.standard_normal(d),
+                 "fc1_w": 0.02 * rng.standard_normal((4 * d, 4 * d)), "fc1_b": 0.02 * rng.standard_normal(4 * d),
+                 "fc2_w": 0.02 * rng.standard_normal((24, 4 * d)), "fc2_b": 0.02 * rng.standard_normal(24)}.items():
+        params["merger." + k] = v
+    _, z_blk, out_blk = O.encode(imgs, params, depth=1)
+    # raster-order tower
+    xs, poss, cu = [], [], [0]
+    for img, (t, gh, gw) in zip(imgs, grids):
+        xs.append(O.raster_patches(img, (t, gh, gw)))
+        hh, ww = np.meshgrid(np.arange(gh), np.arange(gw), indexing="ij")
+        poss.append(np.stack([hh.ravel(), ww.ravel()], 1))
+        cu.append(cu[-1] + gh * gw)
+    z = O.patch_embed(np.concatenate(xs).astype(np.float64), params["patch_w"])
+    z = O.vision_block(z, O.block_params(params, 0), np.array(cu), O.rope_angles(np.concatenate(poss)))
+    outs = []
+    for i, (t, gh, gw) in enumerate(grids):
+        f = O.layer_norm(z[cu[i]:cu[i + 1]], params["merger.ln_w"], params["merger.ln_b"]).reshape(gh, gw, d)
+        g = np.concatenate([f[0::2, 0::2], f[0::2, 1::2], f[1::2, 0::2], f[1::2, 1::2]], -1).reshape(-1, 4 * d)
+        outs.append(O.gelu_erf(g @ params["merger.fc1_w"].T + params["merger.fc1_b"]) @ params["merger.fc2_w"].T
+                    + params["merger.fc2_b"])
+    np.testing.assert_allclose(out_blk, np.concatenate(outs), rtol=1e-9, atol=1e-12)
+
+
+def test_tower_depth_zero_is_patch_embed():
+    rng = np.random.default_rng(16)
+    img = rng.uniform(-1, 1, (1, 3, 56, 56)).astype(np.float32)
+    w = rng.standard_normal((12, 3, 2, 14, 14))
+    g = (1, 4, 4)
+    z = O.vision_forward(O.patchify([img], [g]), {"patch_w": w}, [g], depth=0, heads=3)
+    _, _, perm = O.seq_meta([g])
+    np.testing.assert_allclose(z, _conv3d_reference(img, w)[perm], rtol=1e-12)
