@@ -1,0 +1,284 @@
+// Full bidirectional attention inside each image of a packed batch
+// (block-diagonal by cu_seqlens), head_dim 80, flash-style: keys are
+// streamed in tiles through LDS with an online softmax, so memory is linear
+// in the sequence and nothing of size n^2 is stored.
+//
+// Layouts (written by the q/k/v projection epilogue):
+//   Q, K  [heads][P][80]   bf16/f32, image i's rows start at prow0_i
+//   V^T   [heads][80][P]   (transposed so P.V reads keys contiguously)
+// prow0_i is a multiple of 128 and rows past an image's end are zero.
+// Output O is packed [N][ldo] with head h in columns 80h .. 80h+79.
+//
+// bf16 kernel (gfx950 MFMA, wave64): a workgroup owns 128 query rows of one
+// (image, head); each of its 4 waves owns 32.  Per 64-key tile a wave forms
+// S^T = K . Q^T with v_mfma_f32_32x32x16_bf16 (5 k-steps over the 80 head
+// elements, so no padding), which leaves each lane holding one query column.
+// That register layout is directly the B operand of O^T = V^T . P^T, so P
+// never leaves registers.  The P.V product pads the head to 96 rows (three
+// 32-row MFMA blocks); row 80 of V^T is a row of ones, so O^T row 80
+// accumulates the softmax denominator for free, with the same bf16-rounded P
+// as the numerator.
+#include "qv_internal.h"
+
+namespace qv {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ int find_plan(const PlanEntry* plan, int n_img, int gt) {
+  int lo = 0, hi = n_img - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (plan[mid].qtile0 <= gt) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+constexpr int ABQ = 128;   // query rows per workgroup
+constexpr int ABK = 64;    // keys per tile
+constexpr int KSTR = 88;   // K tile row stride (elements): 176 B keeps 16-byte reads conflict-free
+constexpr int VSTR = 68;   // V^T tile row stride (elements)
+
+__global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a, float scale_log2) {
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][ABK * KSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][kHeadDim * VSTR];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hlf = lane >> 5, l32 = lane & 31;
+  const int head = blockIdx.y;
+  const int gt = blockIdx.x;
+  const PlanEntry pe = a.plan[find_plan(a.plan, a.n_img, gt)];
+  const int row0 = a.cu_seqlens[pe.img];
+  const int n = a.cu_seqlens[pe.img + 1] - row0;
+  const int qbase = (gt - pe.qtile0) * ABQ + wave * 32;
+
+  const uint16_t* Qh = reinterpret_cast<const uint16_t*>(a.q) + (size_t)head * a.P * kHeadDim;
+  const uint16_t* Kh = reinterpret_cast<const uint16_t*>(a.k) + (size_t)head * a.P * kHeadDim;
+  const uint16_t* Vh = reinterpret_cast<const uint16_t*>(a.vt) + (size_t)head * kHeadDim * a.P;
+
+  // B operand of S^T: lane holds query (qbase + l32), head elements 16kk + 8hlf .. +7
+  bf16x8 qf[5];
+  {
+    const uint16_t* qr = Qh + (size_t)(pe.prow0 + qbase + l32) * kHeadDim + 8 * hlf;
+#pragma unroll
+    for (int kk = 0; kk < 5; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qr + 16 * kk);
+  }
+
+  // tile staging: 640 16-byte chunks of K (64 rows x 10) and of V^T (80 rows x 8)
+  uint4 rk[3], rv[3];
+  auto gload = [&](int j) {
+    const int key0 = pe.prow0 + j * ABK;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int id = tid + 256 * i;
+      if (id < 640) {
+        rk[i] = *reinterpret_cast<const uint4*>(Kh + (size_t)(key0 + id / 10) * kHeadDim + (id % 10) * 8);
+        rv[i] = *reinterpret_cast<const uint4*>(Vh + (size_t)(id >> 3) * a.P + key0 + (id & 7) * 8);
+      }
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int id = tid + 256 * i;
+      if (id < 640) {
+        *reinterpret_cast<uint4*>(&sK[buf][(id / 10) * KSTR + (id % 10) * 8]) = rk[i];
+        uint2* vp = reinterpret_cast<uint2*>(&sV[buf][(id >> 3) * VSTR + (id & 7) * 8]);
+        vp[0] = make_uint2(rv[i].x, rv[i].y);
+        vp[1] = make_uint2(rv[i].z, rv[i].w);
+      }
+    }
+  };
+
+  f32x16 o[3];
+#pragma unroll
+  for (int t = 0; t < 3; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
+  float m_run = -INFINITY;
+
+  // constant operand rows 80..95 of the padded V^T block: row 80 = 1, others 0
+  bf16x8 vconst;
+  {
+    const __bf16 one = __builtin_bit_cast(__bf16, (uint16_t)(l32 == 16 ? 0x3F80 : 0));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vconst[e] = one;
+  }
+
+  const int ntiles = (n + ABK - 1) / ABK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int j = 0; j < ntiles; ++j) {
+    const int cur = j & 1;
+    if (j + 1 < ntiles) gload(j + 1);
+
+    f32x16 s[2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[sb][r] = 0.f;
+      const uint16_t* kr = &sK[cur][(32 * sb + l32) * KSTR + 8 * hlf];
+#pragma unroll
+      for (int kk = 0; kk < 5; ++kk)
+        s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kr + 16 * kk), qf[kk],
+                                                         s[sb], 0, 0, 0);
+    }
+    // keys past the image end (last tile only) take no weight
+    if (j * ABK + ABK > n) {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = j * ABK + 32 * sb + 8 * (r >> 2) + 4 * hlf + (r & 3);
+          if (key >= n) s[sb][r] = -INFINITY;
+        }
+    }
+    float mx = s[0][0];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx * scale_log2);
+    const float alpha = exp2f(m_run - m_new);
+    m_run = m_new;
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        bf16x8 pb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          pb[e] = __builtin_bit_cast(__bf16, bf16_rne(exp2f(fmaf(s[sb][8 * s2 + e], scale_log2, -m_new))));
+        const int kofs = 32 * sb + 16 * s2 + 4 * hlf;
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+          const int d = 32 * t + l32;
+          bf16x8 vf;
+          if (t < 2 || l32 < kHeadDim - 64) {
+            const uint16_t* vp = &sV[cur][d * VSTR + kofs];
+            const uint2 lo = *reinterpret_cast<const uint2*>(vp);
+            const uint2 hi = *reinterpret_cast<const uint2*>(vp + 8);
+            vf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+          } else {
+            vf = vconst;
+          }
+          o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, o[t], 0, 0, 0);
+        }
+      }
+    if (j + 1 < ntiles) sstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // O^T row 80 (block 2, local row 16) = register 8 of the lower half-wave
+  const float lsum = __shfl(o[2][8], l32, 64);
+  const float inv = 1.0f / lsum;
+  const int q = qbase + l32;
+  if (q < n) {
+    uint16_t* orow = reinterpret_cast<uint16_t*>(a.o) + (size_t)(row0 + q) * a.ldo + head * kHeadDim;
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * t + 8 * g + 4 * hlf;
+        if (d0 < kHeadDim) {
+          uint2 pk;
+          pk.x = bf16_rne(o[t][4 * g] * inv) | ((uint32_t)bf16_rne(o[t][4 * g + 1] * inv) << 16);
+          pk.y = bf16_rne(o[t][4 * g + 2] * inv) | ((uint32_t)bf16_rne(o[t][4 * g + 3] * inv) << 16);
+          *reinterpret_cast<uint2*>(orow + d0) = pk;
+        }
+      }
+  }
+}
+
+hipError_t attention_bf16(const AttnArgs& a, hipStream_t s) {
+  if (a.total_qtiles == 0) return hipSuccess;
+  const float scale_log2 = 1.4426950408889634f / sqrtf((float)kHeadDim);
+  hipLaunchKernelGGL(k_attn_bf16, dim3((unsigned)a.total_qtiles, (unsigned)a.heads), dim3(256), 0, s, a, scale_log2);
+  return hipGetLastError();
+}
+
+// ============================================================ float32 mode
+// One wave per (64 query rows, head); one query row per lane with the full
+// head vector and accumulator in registers; 32-key tiles in LDS; exact exp.
+constexpr int FBQ = 64, FBK = 32;
+
+__global__ __launch_bounds__(64) void k_attn_f32(AttnArgs a, float scale) {
+  __shared__ float sK[FBK][kHeadDim + 1];
+  __shared__ float sV[kHeadDim][FBK + 1];
+  const int lane = threadIdx.x;
+  const int head = blockIdx.y, gt = blockIdx.x;
+  const PlanEntry pe = a.plan[find_plan(a.plan, a.n_img, gt)];
+  const int row0 = a.cu_seqlens[pe.img];
+  const int n = a.cu_seqlens[pe.img + 1] - row0;
+  const int q = (gt - pe.qtile0) * FBQ + lane;
+  const float* Qh = reinterpret_cast<const float*>(a.q) + (size_t)head * a.P * kHeadDim;
+  const float* Kh = reinterpret_cast<const float*>(a.k) + (size_t)head * a.P * kHeadDim;
+  const float* Vh = reinterpret_cast<const float*>(a.vt) + (size_t)head * kHeadDim * a.P;
+  float qv[kHeadDim], acc[kHeadDim];
+#pragma unroll
+  for (int d = 0; d < kHeadDim; ++d) {
+    qv[d] = Qh[(size_t)(pe.prow0 + q) * kHeadDim + d] * scale;
+    acc[d] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  for (int k0 = 0; k0 < n; k0 += FBK) {
+    for (int i = lane; i < FBK * kHeadDim; i += 64) {
+      const int r = i / kHeadDim, d = i % kHeadDim;
+      sK[r][d] = Kh[(size_t)(pe.prow0 + k0 + r) * kHeadDim + d];
+      const int dd = i / FBK, c = i % FBK;
+      sV[dd][c] = Vh[(size_t)dd * a.P + pe.prow0 + k0 + c];
+    }
+    __syncthreads();
+    const int nk = n - k0 < FBK ? n - k0 : FBK;
+    float sc[FBK];
+    float mt = -INFINITY;
+    for (int c = 0; c < FBK; ++c) {
+      float dot = 0.f;
+#pragma unroll
+      for (int d = 0; d < kHeadDim; ++d) dot = fmaf(qv[d], sK[c][d], dot);
+      sc[c] = c < nk ? dot : -INFINITY;
+      mt = fmaxf(mt, sc[c]);
+    }
+    const float mn = fmaxf(m, mt);
+    const float corr = expf(m - mn);
+    l *= corr;
+#pragma unroll
+    for (int d = 0; d < kHeadDim; ++d) acc[d] *= corr;
+    for (int c = 0; c < FBK; ++c) {
+      const float p = expf(sc[c] - mn);
+      l += p;
+#pragma unroll
+      for (int d = 0; d < kHeadDim; ++d) acc[d] = fmaf(p, sV[d][c], acc[d]);
+    }
+    m = mn;
+    __syncthreads();
+  }
+  if (q < n) {
+    float* orow = reinterpret_cast<float*>(a.o) + (size_t)(row0 + q) * a.ldo + head * kHeadDim;
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int d = 0; d < kHeadDim; ++d) orow[d] = acc[d] * inv;
+  }
+}
+
+hipError_t attention_f32(const AttnArgs& a, hipStream_t s) {
+  if (a.total_qtiles == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_attn_f32, dim3((unsigned)a.total_qtiles, (unsigned)a.heads), dim3(64), 0, s, a,
+                     1.0f / sqrtf((float)kHeadDim));
+  return hipGetLastError();
+}
+
+}  // namespace qv

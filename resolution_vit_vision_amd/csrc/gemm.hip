@@ -1,0 +1,426 @@
+// C = A . B^T on gfx950 matrix cores (bf16 operands, f32 accumulation) with
+// fused epilogues, plus a plain float32 tiled kernel for the correctness mode.
+//
+// A is [M][lda] (activations), B is [N][ldb] (a Linear weight, [out][in]);
+// both are K-contiguous, so one 16-byte global load moves 8 consecutive k of
+// one row.  Tiles of BK = 64 are staged through LDS with an XOR swizzle of
+// the 16-byte chunks (chunk ^ (row & 7)) so that the per-lane 16-byte reads of
+// the v_mfma_f32_32x32x16_bf16 operand pattern (32 rows, two k-chunks) spread
+// over all banks.  Global loads for tile k+1 are issued before the MFMAs of
+// tile k and written to the other LDS buffer after them (one barrier per
+// tile).
+#include "qv_internal.h"
+
+namespace qv {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ uint16_t bf16_bits(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float act_apply(Act a, float u) {
+  if (a == Act::QuickGelu) return u / (1.0f + __expf(-1.702f * u));
+  if (a == Act::GeluErf) return 0.5f * u * (1.0f + erff(u * 0.70710678118654752440f));
+  return u;
+}
+
+// Output position of accumulator register r of MFMA block (fm, fn) for `lane`.
+#define QV_ACC_ROW(wm0, fm, r, lane) ((wm0) + (fm) * 32 + 8 * ((r) >> 2) + 4 * ((lane) >> 5) + ((r) & 3))
+#define QV_ACC_COL(wn0, fn, lane) ((wn0) + (fn) * 32 + ((lane) & 31))
+
+// ------------------------------------------------------------- epilogues
+struct EpiStoreF32 {
+  float* C; int ldc; const float* bias;
+  template <int FM, int FN>
+  __device__ void apply(f32x16 (&acc)[FM][FN], int wm0, int wn0, int lane, int M, int N) const {
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      const int col = QV_ACC_COL(wn0, fn, lane);
+      if (col >= N) continue;
+      const float bb = bias ? bias[col] : 0.f;
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = QV_ACC_ROW(wm0, fm, r, lane);
+          if (row < M) C[(size_t)row * ldc + col] = acc[fm][fn][r] + bb;
+        }
+    }
+  }
+};
+
+struct EpiResidF32 {
+  float* Z; int ldz; const float* bias;
+  template <int FM, int FN>
+  __device__ void apply(f32x16 (&acc)[FM][FN], int wm0, int wn0, int lane, int M, int N) const {
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      const int col = QV_ACC_COL(wn0, fn, lane);
+      if (col >= N) continue;
+      const float bb = bias[col];
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = QV_ACC_ROW(wm0, fm, r, lane);
+          if (row < M) {
+            float* p = Z + (size_t)row * ldz + col;
+            *p = *p + (acc[fm][fn][r] + bb);
+          }
+        }
+    }
+  }
+};
+
+struct EpiActBf16 {
+  uint16_t* C; int ldc; const float* bias; Act act;
+  template <int FM, int FN>
+  __device__ void apply(f32x16 (&acc)[FM][FN], int wm0, int wn0, int lane, int M, int N) const {
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      const int col = QV_ACC_COL(wn0, fn, lane);
+      if (col >= N) continue;
+      const float bb = bias[col];
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = QV_ACC_ROW(wm0, fm, r, lane);
+          if (row < M) C[(size_t)row * ldc + col] = bf16_bits(act_apply(act, acc[fm][fn][r] + bb));
+        }
+    }
+  }
+};
+
+// q/k/v projection.  The GEMM's virtual column v runs over [0, 3 dim).  In
+// the q and k thirds every aligned group of 64 virtual columns holds 32
+// rotation pairs: virtual column 64g + c (c < 32) is element j and 64g + 32 + c
+// is element j + 40 of the same head, pair index 32g + c = 40 head + j.  The
+// B-row loader applies the same map, so both halves of a pair land in the
+// same lane (MFMA blocks fn and fn + 1) and the rotation needs no exchange.
+// The v third is stored transposed per head ([head][80][P]) for the
+// attention kernel's P.V product.
+__device__ __forceinline__ int qkv_weight_row(int v, int dim) {
+  if (v >= 2 * dim) return v;
+  const int region = v >= dim ? 1 : 0;
+  const int vv = v - region * dim;
+  const int within = vv & 63;
+  const int pair = ((vv >> 6) << 5) + (within & 31);
+  const int head = pair / (kHeadDim / 2), j = pair % (kHeadDim / 2);
+  return region * dim + head * kHeadDim + j + (within >> 5) * (kHeadDim / 2);
+}
+
+struct RowMapIdentity {
+  __device__ int operator()(int r) const { return r; }
+};
+struct RowMapQkv {
+  int dim;
+  __device__ int operator()(int r) const { return qkv_weight_row(r, dim); }
+};
+
+struct EpiQkv {
+  QkvOut o; const float* bias;
+  template <int FM, int FN>
+  __device__ void apply(f32x16 (&acc)[FM][FN], int wm0, int wn0, int lane, int M, int N) const {
+    const int dim = o.dim;
+    if (wn0 < 2 * dim) {
+      // the wave's columns are whole 64-groups of the q or k third
+#pragma unroll
+      for (int fp = 0; fp < FN; fp += 2) {
+        const int v = QV_ACC_COL(wn0, fp, lane);
+        const int region = v >= dim ? 1 : 0;
+        const int vv = v - region * dim;
+        const int pair = ((vv >> 6) << 5) + (vv & 31);
+        const int head = pair / (kHeadDim / 2), j = pair % (kHeadDim / 2);
+        const int f0 = region * dim + head * kHeadDim + j;
+        const float b0 = bias[f0], b1 = bias[f0 + kHeadDim / 2];
+        uint16_t* dst = reinterpret_cast<uint16_t*>(region ? o.k : o.q) + (size_t)head * o.P * kHeadDim + j;
+        const int fi = j < kRopeFreqs ? j : j - kRopeFreqs;
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = QV_ACC_ROW(wm0, fm, r, lane);
+            if (row >= M) continue;
+            const int2 ti = o.tokinfo[row];
+            const int p = j < kRopeFreqs ? (ti.x & 0xFFFF) : (ti.x >> 16);
+            const float2 cs = o.rope[p * kRopeFreqs + fi];
+            const float x0 = acc[fm][fp][r] + b0, x1 = acc[fm][fp + 1][r] + b1;
+            uint16_t* d = dst + (size_t)ti.y * kHeadDim;
+            d[0] = bf16_bits(x0 * cs.x - x1 * cs.y);
+            d[kHeadDim / 2] = bf16_bits(x1 * cs.x + x0 * cs.y);
+          }
+      }
+    } else {
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int col = QV_ACC_COL(wn0, fn, lane);
+        if (col >= N) continue;
+        const int f = col - 2 * dim;
+        const int head = f / kHeadDim, dd = f % kHeadDim;
+        const float bb = bias[col];
+        uint16_t* dst = reinterpret_cast<uint16_t*>(o.vt) + ((size_t)head * kHeadDim + dd) * o.P;
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = QV_ACC_ROW(wm0, fm, r, lane);
+            if (row < M) dst[o.tokinfo[row].y] = bf16_bits(acc[fm][fn][r] + bb);
+          }
+      }
+    }
+  }
+};
+
+// ------------------------------------------------------------------ kernel
+template <int BM, int BN, int WM, int WN, class Epi, class RowMap>
+__global__ __launch_bounds__(256) void k_gemm_bf16(const uint16_t* __restrict__ A, int lda,
+                                                   const uint16_t* __restrict__ B, int ldb, int M, int N, int K,
+                                                   Epi epi, RowMap rmap) {
+  constexpr int BK = 64;
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 32, FN = TN / 32;
+  constexpr int ACH = BM * 8 / 256, BCH = BN * 8 / 256;
+  static_assert(WM * WN == 4, "four waves");
+  static_assert(FM >= 1 && FN >= 1 && ACH >= 1 && BCH >= 1, "tile too small");
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * BK];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int tiles_n = (N + BN - 1) / BN;
+  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const uint16_t* ap[ACH];
+  int aoff[ACH], akc[ACH];
+  bool aok[ACH];
+#pragma unroll
+  for (int i = 0; i < ACH; ++i) {
+    const int id = tid + 256 * i, r = id >> 3, c = id & 7;
+    const int g = m0 + r;
+    aok[i] = g < M;
+    ap[i] = A + (size_t)(aok[i] ? g : 0) * lda + c * 8;
+    akc[i] = c * 8;
+    aoff[i] = r * BK + ((c ^ (r & 7)) << 3);
+  }
+  const uint16_t* bp[BCH];
+  int boff[BCH], bkc[BCH];
+  bool bok[BCH];
+#pragma unroll
+  for (int i = 0; i < BCH; ++i) {
+    const int id = tid + 256 * i, r = id >> 3, c = id & 7;
+    const int g = n0 + r;
+    bok[i] = g < N;
+    bp[i] = B + (size_t)rmap(bok[i] ? g : 0) * ldb + c * 8;
+    bkc[i] = c * 8;
+    boff[i] = r * BK + ((c ^ (r & 7)) << 3);
+  }
+
+  uint4 ra[ACH], rb[BCH];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < ACH; ++i)
+      ra[i] = (aok[i] && k0 + akc[i] < K) ? *reinterpret_cast<const uint4*>(ap[i] + k0) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < BCH; ++i)
+      rb[i] = (bok[i] && k0 + bkc[i] < K) ? *reinterpret_cast<const uint4*>(bp[i] + k0) : make_uint4(0, 0, 0, 0);
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) *reinterpret_cast<uint4*>(&sA[buf][aoff[i]]) = ra[i];
+#pragma unroll
+    for (int i = 0; i < BCH; ++i) *reinterpret_cast<uint4*>(&sB[buf][boff[i]]) = rb[i];
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int KT = (K + BK - 1) / BK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  const int arow = wm * TM + (lane & 31), brow = wn * TN + (lane & 31);
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < KT) gload((kt + 1) * BK);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int c = kk * 2 + (lane >> 5);
+      bf16x8 a[FM], b[FN];
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        const int r = arow + fm * 32;
+        a[fm] = *reinterpret_cast<const bf16x8*>(&sA[cur][r * BK + ((c ^ (r & 7)) << 3)]);
+      }
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int r = brow + fn * 32;
+        b[fn] = *reinterpret_cast<const bf16x8*>(&sB[cur][r * BK + ((c ^ (r & 7)) << 3)]);
+      }
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[fm], b[fn], acc[fm][fn], 0, 0, 0);
+    }
+    if (kt + 1 < KT) sstore(cur ^ 1);
+    __syncthreads();
+  }
+  epi.apply(acc, m0 + wm * TM, n0 + wn * TN, lane, M, N);
+}
+
+template <class Epi, class RowMap>
+static hipError_t run_bf16(const void* A, int lda, const void* B, int ldb, int M, int N, int K, const Epi& epi,
+                           RowMap rmap, hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  constexpr int BM = 128, BN = 128;
+  const unsigned tiles = (unsigned)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
+  hipLaunchKernelGGL((k_gemm_bf16<BM, BN, 2, 2, Epi, RowMap>), dim3(tiles), dim3(256), 0, s,
+                     reinterpret_cast<const uint16_t*>(A), lda, reinterpret_cast<const uint16_t*>(B), ldb, M, N, K,
+                     epi, rmap);
+  return hipGetLastError();
+}
+
+hipError_t gemm_bf16_store_f32(const void* A, int lda, const void* B, int ldb, int M, int N, int K,
+                               const float* bias, float* C, int ldc, hipStream_t s) {
+  return run_bf16(A, lda, B, ldb, M, N, K, EpiStoreF32{C, ldc, bias}, RowMapIdentity{}, s);
+}
+hipError_t gemm_bf16_resid_f32(const void* A, int lda, const void* B, int ldb, int M, int N, int K,
+                               const float* bias, float* Z, int ldz, hipStream_t s) {
+  return run_bf16(A, lda, B, ldb, M, N, K, EpiResidF32{Z, ldz, bias}, RowMapIdentity{}, s);
+}
+hipError_t gemm_bf16_act_bf16(const void* A, int lda, const void* B, int ldb, int M, int N, int K,
+                              const float* bias, Act act, void* C, int ldc, hipStream_t s) {
+  return run_bf16(A, lda, B, ldb, M, N, K, EpiActBf16{reinterpret_cast<uint16_t*>(C), ldc, bias, act},
+                  RowMapIdentity{}, s);
+}
+hipError_t gemm_bf16_qkv(const void* A, int lda, const void* B, int ldb, int M, int K, const float* bias,
+                         const QkvOut& o, hipStream_t s) {
+  return run_bf16(A, lda, B, ldb, M, 3 * o.dim, K, EpiQkv{o, bias}, RowMapQkv{o.dim}, s);
+}
+
+// =================================================== float32 (correctness)
+// 64 x 64 output tile, 256 threads with 4 x 4 outputs each, BK = 16.
+template <class Epi>
+__global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, int lda, const float* __restrict__ B,
+                                                  int ldb, int M, int N, int K, Epi epi) {
+  __shared__ float sA[16][65];
+  __shared__ float sB[16][65];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int tiles_n = (N + 63) / 64;
+  const int m0 = (blockIdx.x / tiles_n) * 64, n0 = (blockIdx.x % tiles_n) * 64;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += 16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int id = tid + 256 * i, r = id >> 4, k = id & 15;
+      const int gm = m0 + r, gn = n0 + r, gk = k0 + k;
+      sA[k][r] = (gm < M && gk < K) ? A[(size_t)gm * lda + gk] : 0.f;
+      sB[k][r] = (gn < N && gk < K) ? B[(size_t)gn * ldb + gk] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { a[i] = sA[k][ty + 16 * i]; b[i] = sB[k][tx + 16 * i]; }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = m0 + ty + 16 * i, col = n0 + tx + 16 * j;
+      if (row < M && col < N) epi(row, col, acc[i][j]);
+    }
+}
+
+struct F32Store {
+  float* C; int ldc; const float* bias;
+  __device__ void operator()(int r, int c, float v) const { C[(size_t)r * ldc + c] = v + (bias ? bias[c] : 0.f); }
+};
+struct F32Resid {
+  float* Z; int ldz; const float* bias;
+  __device__ void operator()(int r, int c, float v) const {
+    float* p = Z + (size_t)r * ldz + c;
+    *p = *p + (v + bias[c]);
+  }
+};
+struct F32Act {
+  float* C; int ldc; const float* bias; Act act;
+  __device__ void operator()(int r, int c, float v) const { C[(size_t)r * ldc + c] = act_apply(act, v + bias[c]); }
+};
+
+template <class Epi>
+static hipError_t run_f32(const float* A, int lda, const float* B, int ldb, int M, int N, int K, const Epi& e,
+                          hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  const unsigned tiles = (unsigned)(((M + 63) / 64) * ((N + 63) / 64));
+  hipLaunchKernelGGL(k_gemm_f32<Epi>, dim3(tiles), dim3(256), 0, s, A, lda, B, ldb, M, N, K, e);
+  return hipGetLastError();
+}
+
+hipError_t gemm_f32_store(const float* A, int lda, const float* B, int ldb, int M, int N, int K, const float* bias,
+                          float* C, int ldc, hipStream_t s) {
+  return run_f32(A, lda, B, ldb, M, N, K, F32Store{C, ldc, bias}, s);
+}
+hipError_t gemm_f32_resid(const float* A, int lda, const float* B, int ldb, int M, int N, int K, const float* bias,
+                          float* Z, int ldz, hipStream_t s) {
+  return run_f32(A, lda, B, ldb, M, N, K, F32Resid{Z, ldz, bias}, s);
+}
+hipError_t gemm_f32_act(const float* A, int lda, const float* B, int ldb, int M, int N, int K, const float* bias,
+                        Act act, float* C, int ldc, hipStream_t s) {
+  return run_f32(A, lda, B, ldb, M, N, K, F32Act{C, ldc, bias, act}, s);
+}
+
+// qkv [M][3 dim] (bias already added) -> rotated q, k and transposed v in the
+// padded per-head layouts.  One thread per (row, pair) for q and k and per
+// (row, element) for v.
+__global__ __launch_bounds__(256) void k_rope_scatter_f32(const float* __restrict__ qkv, int M, QkvOut o) {
+  const int dim = o.dim;
+  const int per_row = 2 * dim;  // dim/2 pairs of q, dim/2 pairs of k, dim elements of v
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)M * per_row) return;
+  const int row = (int)(gid / per_row), c = (int)(gid % per_row);
+  const int2 ti = o.tokinfo[row];
+  const float* src = qkv + (size_t)row * 3 * dim;
+  if (c < dim) {
+    const int region = c / (dim / 2), pair = c % (dim / 2);
+    const int head = pair / (kHeadDim / 2), j = pair % (kHeadDim / 2);
+    const int f0 = region * dim + head * kHeadDim + j;
+    const float x0 = src[f0], x1 = src[f0 + kHeadDim / 2];
+    const int p = j < kRopeFreqs ? (ti.x & 0xFFFF) : (ti.x >> 16);
+    const float2 cs = o.rope[p * kRopeFreqs + (j < kRopeFreqs ? j : j - kRopeFreqs)];
+    float* dst = reinterpret_cast<float*>(region ? o.k : o.q) + ((size_t)head * o.P + ti.y) * kHeadDim + j;
+    dst[0] = x0 * cs.x - x1 * cs.y;
+    dst[kHeadDim / 2] = x1 * cs.x + x0 * cs.y;
+  } else {
+    const int f = c - dim;
+    const int head = f / kHeadDim, dd = f % kHeadDim;
+    reinterpret_cast<float*>(o.vt)[((size_t)head * kHeadDim + dd) * o.P + ti.y] = src[2 * dim + f];
+  }
+}
+
+hipError_t rope_scatter_f32(const float* qkv, int M, const float*, const QkvOut& o, hipStream_t s) {
+  const int64_t n = (int64_t)M * 2 * o.dim;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_rope_scatter_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, qkv, M, o);
+  return hipGetLastError();
+}
+
+}  // namespace qv

@@ -1,0 +1,218 @@
+// Memory-bound kernels of the encoder: patch gather, per-token metadata,
+// rotary table, zero fill and LayerNorm.  All written for wave64 (gfx950).
+#include "qv_internal.h"
+
+namespace qv {
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ------------------------------------------------------------------ patchify
+// One thread writes 8 consecutive elements of one output row.  Rows of an
+// image follow the merge-group order: slot s -> (t, block row, block col,
+// dy, dx) with dx fastest; element e -> (channel, temporal slot, row, col).
+__global__ __launch_bounds__(256) void k_patchify(const float* __restrict__ pixels, PatchChunk c, int patch,
+                                                  int temporal, void* __restrict__ out, int bf16, int ld,
+                                                  int patch_dim) {
+  const int img = blockIdx.y;
+  if (img >= c.count) return;
+  const PatchImg d = c.d[img];
+  const int chunks = patch_dim / 8;
+  const int64_t n = (int64_t)d.t * d.gh * d.gw;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= n * chunks) return;
+  const int64_t s = gid / chunks;
+  const int e0 = (int)(gid % chunks) * 8;
+  const int hw = d.gh * d.gw;
+  const int tt = (int)(s / hw);
+  const int rem = (int)(s % hw);
+  const int blk = rem >> 2, q = rem & 3;
+  const int half_w = d.gw >> 1;
+  const int h = 2 * (blk / half_w) + (q >> 1);
+  const int w = 2 * (blk % half_w) + (q & 1);
+  const int pp = patch * patch;
+  float v[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int e = e0 + u;
+    const int ch = e / (temporal * pp);
+    const int r1 = e % (temporal * pp);
+    const int tau = r1 / pp;
+    const int r2 = r1 % pp;
+    const int i = r2 / patch, j = r2 % patch;
+    int f = temporal * tt + tau;
+    f = f < d.frames - 1 ? f : d.frames - 1;
+    const int64_t src = d.offset + (((int64_t)f * d.channels + ch) * d.height + (int64_t)patch * h + i) * d.width +
+                        (int64_t)patch * w + j;
+    v[u] = pixels[src];
+  }
+  const int64_t row = d.row0 + s;
+  if (bf16) {
+    uint4 pk;
+    pk.x = f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+    pk.y = f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+    pk.z = f32_to_bf16_rne(v[4]) | ((uint32_t)f32_to_bf16_rne(v[5]) << 16);
+    pk.w = f32_to_bf16_rne(v[6]) | ((uint32_t)f32_to_bf16_rne(v[7]) << 16);
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + row * ld + e0) = pk;
+  } else {
+    float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + row * ld + e0);
+    o[0] = make_float4(v[0], v[1], v[2], v[3]);
+    o[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
+hipError_t launch_patchify(const float* pixels, const PatchChunk& c, int patch, int temporal, void* out, bool bf16,
+                           int ld, int patch_dim, int64_t rows_in_chunk_max, hipStream_t s) {
+  const int64_t threads = rows_in_chunk_max * (patch_dim / 8);
+  dim3 grid((unsigned)((threads + 255) / 256), (unsigned)c.count);
+  hipLaunchKernelGGL(k_patchify, grid, dim3(256), 0, s, pixels, c, patch, temporal, out, bf16 ? 1 : 0, ld,
+                     patch_dim);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------- token metadata
+// tokinfo[row] = { h | (w << 16), padded row } for every packed row.
+__global__ __launch_bounds__(256) void k_setup_tokens(DescChunk c, int2* __restrict__ tokinfo) {
+  const int img = blockIdx.y;
+  if (img >= c.count) return;
+  const ImgDesc d = c.d[img];
+  const int s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (s >= d.n) return;
+  const int hw = d.gh * d.gw;
+  const int rem = s % hw;
+  const int blk = rem >> 2, q = rem & 3;
+  const int half_w = d.gw >> 1;
+  const int h = 2 * (blk / half_w) + (q >> 1);
+  const int w = 2 * (blk % half_w) + (q & 1);
+  tokinfo[d.row0 + s] = make_int2(h | (w << 16), d.prow0 + s);
+}
+
+hipError_t launch_setup_tokens(const DescChunk& c, int2* tokinfo, hipStream_t s) {
+  int nmax = 0;
+  for (int i = 0; i < c.count; ++i) nmax = c.d[i].n > nmax ? c.d[i].n : nmax;
+  if (nmax == 0) return hipSuccess;
+  dim3 grid((unsigned)((nmax + 255) / 256), (unsigned)c.count);
+  hipLaunchKernelGGL(k_setup_tokens, grid, dim3(256), 0, s, c, tokinfo);
+  return hipGetLastError();
+}
+
+struct PlanChunk {
+  int32_t count;
+  int32_t first;
+  PlanEntry e[kDescChunk];
+};
+
+__global__ void k_setup_plan(PlanChunk c, PlanEntry* __restrict__ plan) {
+  const int i = threadIdx.x;
+  if (i < c.count) plan[c.first + i] = c.e[i];
+}
+
+hipError_t launch_setup_plan(const PlanEntry* host_plan_chunk, int count, int first, PlanEntry* plan,
+                             hipStream_t s) {
+  PlanChunk c;
+  c.count = count;
+  c.first = first;
+  for (int i = 0; i < count; ++i) c.e[i] = host_plan_chunk[i];
+  hipLaunchKernelGGL(k_setup_plan, dim3(1), dim3(64), 0, s, c, plan);
+  return hipGetLastError();
+}
+
+// rope[p][k] = (cos, sin)(p * theta^(-k/20)), evaluated in double, stored f32.
+__global__ __launch_bounds__(256) void k_rope_table(float2* __restrict__ tab, int positions, double theta) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= positions * kRopeFreqs) return;
+  const int p = i / kRopeFreqs, k = i % kRopeFreqs;
+  const double omega = pow(theta, -(double)k / (double)kRopeFreqs);
+  const double a = (double)p * omega;
+  tab[i] = make_float2((float)cos(a), (float)sin(a));
+}
+
+hipError_t launch_rope_table(float2* tab, int positions, float theta, hipStream_t s) {
+  const int n = positions * kRopeFreqs;
+  hipLaunchKernelGGL(k_rope_table, dim3((n + 255) / 256), dim3(256), 0, s, tab, positions, (double)theta);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void k_zero(uint4* __restrict__ p, size_t n16) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) p[i] = make_uint4(0, 0, 0, 0);
+}
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
+  const size_t n16 = bytes / 16;  // callers pass 16-byte multiples
+  if (n16 == 0) return hipSuccess;
+  size_t blocks = (n16 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_zero, dim3((unsigned)blocks), dim3(256), 0, s, reinterpret_cast<uint4*>(p), n16);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------- LayerNorm
+// One wave64 per row of NV*256 floats: each lane holds NV float4.  Statistics
+// in float32: mean, then the mean of squared deviations (two passes over
+// registers), y = (x - mean) * rsqrt(var + eps) * g + b.
+template <int NV>
+__global__ __launch_bounds__(256) void k_layernorm(const float* __restrict__ x, const float* __restrict__ g,
+                                                   const float* __restrict__ b, void* __restrict__ y, int bf16,
+                                                   int rows, float eps) {
+  constexpr int D = NV * 256;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const float4* xr = reinterpret_cast<const float4*>(x + (size_t)row * D);
+  float4 v[NV];
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    v[i] = xr[i * 64 + lane];
+    sum += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
+  const float mean = sum * (1.0f / D);
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    v[i].x -= mean; v[i].y -= mean; v[i].z -= mean; v[i].w -= mean;
+    sq += (v[i].x * v[i].x + v[i].y * v[i].y) + (v[i].z * v[i].z + v[i].w * v[i].w);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
+  const float rstd = rsqrtf(sq * (1.0f / D) + eps);
+  const float4* g4 = reinterpret_cast<const float4*>(g);
+  const float4* b4 = reinterpret_cast<const float4*>(b);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const float4 gg = g4[i * 64 + lane], bb = b4[i * 64 + lane];
+    const float o0 = v[i].x * rstd * gg.x + bb.x, o1 = v[i].y * rstd * gg.y + bb.y;
+    const float o2 = v[i].z * rstd * gg.z + bb.z, o3 = v[i].w * rstd * gg.w + bb.w;
+    if (bf16) {
+      uint2 pk;
+      pk.x = f32_to_bf16_rne(o0) | ((uint32_t)f32_to_bf16_rne(o1) << 16);
+      pk.y = f32_to_bf16_rne(o2) | ((uint32_t)f32_to_bf16_rne(o3) << 16);
+      reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(y) + (size_t)row * D)[i * 64 + lane] = pk;
+    } else {
+      reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + (size_t)row * D)[i * 64 + lane] =
+          make_float4(o0, o1, o2, o3);
+    }
+  }
+}
+
+hipError_t launch_layernorm(const float* x, const float* g, const float* b, void* y, bool bf16, int rows, int dim,
+                            float eps, hipStream_t s) {
+  dim3 grid((unsigned)((rows + 3) / 4));
+  const int nv = dim / 256;
+  switch (nv) {
+    case 4: hipLaunchKernelGGL(k_layernorm<4>, grid, dim3(256), 0, s, x, g, b, y, bf16 ? 1 : 0, rows, eps); break;
+    case 5: hipLaunchKernelGGL(k_layernorm<5>, grid, dim3(256), 0, s, x, g, b, y, bf16 ? 1 : 0, rows, eps); break;
+    case 6: hipLaunchKernelGGL(k_layernorm<6>, grid, dim3(256), 0, s, x, g, b, y, bf16 ? 1 : 0, rows, eps); break;
+    case 8: hipLaunchKernelGGL(k_layernorm<8>, grid, dim3(256), 0, s, x, g, b, y, bf16 ? 1 : 0, rows, eps); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace qv

@@ -1,0 +1,113 @@
+// Internal interfaces between the host orchestration and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qv {
+
+constexpr int kHeadDim = 80;       // attention kernels are written for 80-wide heads
+constexpr int kRopeFreqs = kHeadDim / 4;
+constexpr int kSeqAlign = 128;     // each image's rows in Q/K/V^T start on this multiple
+
+// Per-image description computed on the host from grid_thw.
+struct ImgDesc {
+  int32_t row0;   // first packed row (cu_seqlens[i])
+  int32_t n;      // patches T*gh*gw
+  int32_t t, gh, gw;
+  int32_t prow0;  // first row in the padded attention layout
+};
+
+constexpr int kDescChunk = 32;
+struct DescChunk {
+  int32_t count;
+  int32_t first;  // index of d[0] in the full list
+  ImgDesc d[kDescChunk];
+};
+
+// One entry of the attention work plan, images sorted by length, longest first.
+struct PlanEntry {
+  int32_t img;        // image index (into cu_seqlens)
+  int32_t prow0;      // padded row start
+  int32_t qtile0;     // first global q-tile of this image
+  int32_t reserved;
+};
+
+// Patchify: one image per chunk entry.
+struct PatchImg {
+  int64_t offset;
+  int32_t frames, channels, height, width;
+  int32_t t, gh, gw, row0;
+};
+constexpr int kPatchChunk = 16;
+struct PatchChunk {
+  int32_t count;
+  PatchImg d[kPatchChunk];
+};
+
+enum class Act : int { None = 0, QuickGelu = 1, GeluErf = 2 };
+
+// ---- launchers (return hipGetLastError()) ----
+hipError_t launch_patchify(const float* pixels, const PatchChunk& c, int patch, int temporal, void* out,
+                           bool bf16, int ld, int patch_dim, int64_t rows_in_chunk_max, hipStream_t s);
+
+hipError_t launch_setup_tokens(const DescChunk& c, int2* tokinfo, hipStream_t s);
+hipError_t launch_setup_plan(const PlanEntry* host_plan_chunk, int count, int first, PlanEntry* plan,
+                             hipStream_t s);
+hipError_t launch_rope_table(float2* tab, int positions, float theta, hipStream_t s);
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+
+hipError_t launch_layernorm(const float* x, const float* g, const float* b, void* y, bool bf16, int rows,
+                            int dim, float eps, hipStream_t s);
+
+// C = A . B^T with an epilogue (bf16 operands, MFMA).
+struct QkvOut {
+  void* q;         // [heads][P][80]
+  void* k;         // [heads][P][80]
+  void* vt;        // [heads][80][P]
+  const int2* tokinfo;
+  const float2* rope;  // [positions][20] (cos, sin)
+  int P;           // padded rows
+  int dim;         // q/k/v width (heads*80)
+};
+
+hipError_t gemm_bf16_store_f32(const void* A, int lda, const void* B, int ldb, int M, int N, int K,
+                               const float* bias, float* C, int ldc, hipStream_t s);
+hipError_t gemm_bf16_resid_f32(const void* A, int lda, const void* B, int ldb, int M, int N, int K,
+                               const float* bias, float* Z, int ldz, hipStream_t s);
+hipError_t gemm_bf16_act_bf16(const void* A, int lda, const void* B, int ldb, int M, int N, int K,
+                              const float* bias, Act act, void* C, int ldc, hipStream_t s);
+hipError_t gemm_bf16_qkv(const void* A, int lda, const void* B, int ldb, int M, int K, const float* bias,
+                         const QkvOut& o, hipStream_t s);
+
+// float32 counterparts (correctness mode).
+hipError_t gemm_f32_store(const float* A, int lda, const float* B, int ldb, int M, int N, int K,
+                          const float* bias, float* C, int ldc, hipStream_t s);
+hipError_t gemm_f32_resid(const float* A, int lda, const float* B, int ldb, int M, int N, int K,
+                          const float* bias, float* Z, int ldz, hipStream_t s);
+hipError_t gemm_f32_act(const float* A, int lda, const float* B, int ldb, int M, int N, int K,
+                        const float* bias, Act act, float* C, int ldc, hipStream_t s);
+hipError_t rope_scatter_f32(const float* qkv, int M, const float* bias_unused, const QkvOut& o,
+                            hipStream_t s);
+
+// Varlen attention over the padded layout; O packed [N][ldo].
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* vt;
+  void* o;
+  int ldo;
+  const int32_t* cu_seqlens;
+  const PlanEntry* plan;
+  int n_img;
+  int P;
+  int heads;
+  int total_qtiles;
+};
+hipError_t attention_bf16(const AttnArgs& a, hipStream_t s);
+hipError_t attention_f32(const AttnArgs& a, hipStream_t s);
+constexpr int kAttnBQ_bf16 = 128;
+constexpr int kAttnBQ_f32 = 64;
+
+}  // namespace qv

@@ -1,0 +1,147 @@
+"""Host side of the C ABI (no GPU needed): the library loads and exports every
+symbol include/qv.h declares, the integer work is bit-exact with the oracle,
+and argument validation returns the documented status without launching."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import resolution_vit_vision_amd as qv
+from resolution_vit_vision_amd import _abi
+from oracle import qv_oracle as O
+
+
+def test_library_exports_every_header_symbol():
+    L = qv.lib()
+    names = qv.header_functions()
+    assert len(names) >= 10
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+    assert L.qv_abi_version() == 1
+
+
+def test_grid_params_default():
+    p = _abi.GridParams()
+    qv.lib().qv_grid_params_default(ctypes.byref(p))
+    assert (p.patch, p.merge, p.temporal, p.min_pixels, p.max_pixels) == (14, 2, 2, 3136, 12845056)
+
+
+def _abi_grid(h, w, f=1):
+    g = (ctypes.c_int32 * 3)()
+    oh, ow = ctypes.c_int64(), ctypes.c_int64()
+    st = qv.lib().qv_smart_resize_grid(h, w, f, None, ctypes.byref(oh), ctypes.byref(ow), g)
+    return st, (oh.value, ow.value, (g[0], g[1], g[2]))
+
+
+def test_smart_resize_bit_exact_with_oracle():
+    rng = np.random.default_rng(0)
+    cases = [(h, w) for h in range(1, 2001, 11) for w in range(1, 2001, 19)]
+    cases += [tuple(int(x) for x in r) for r in rng.integers(1, 20000, size=(4000, 2))]
+    cases += [(70, 112), (98, 112), (3584, 3584), (3585, 3584), (1, 1), (27, 29), (20000, 28), (28, 1000000), (5, 3000000)]
+    n_err = 0
+    for h, w in cases:
+        for f in (1, 2, 3):
+            st, got = _abi_grid(h, w, f)
+            try:
+                want = O.grid_thw(h, w, f)
+            except ValueError:
+                assert st == _abi.QV_ERR_BUDGET, (h, w, st)
+                n_err += 1
+                continue
+            assert st == _abi.QV_OK, (h, w, qv.lib().qv_last_error())
+            assert got == want, (h, w, f, got, want)
+    assert n_err > 0  # the extreme-aspect branch was exercised
+
+
+def test_smart_resize_errors():
+    g = (ctypes.c_int32 * 3)()
+    L = qv.lib()
+    assert L.qv_smart_resize_grid(0, 10, 1, None, None, None, g) == _abi.QV_ERR_SHAPE
+    assert L.qv_smart_resize_grid(10, 10, 0, None, None, None, g) == _abi.QV_ERR_SHAPE
+    assert L.qv_smart_resize_grid(10, 10, 1, None, None, None, None) == _abi.QV_ERR_NULL
+    assert b"NULL" in L.qv_last_error()
+    assert L.qv_smart_resize_grid(28, 1000000, 1, None, None, None, g) == _abi.QV_ERR_BUDGET
+
+
+def test_seq_meta_bit_exact_with_oracle():
+    rng = np.random.default_rng(1)
+    lists = [[(1, 4, 4)], [(1, 48, 48)] * 4, [(2, 6, 10), (1, 2, 2), (3, 4, 8)],
+             [(1, int(a), int(b)) for a, b in 2 * rng.integers(1, 40, size=(16, 2))]]
+    for grids in lists:
+        cu, pos, perm = qv.seq_meta(grids)
+        cu_o, pos_o, perm_o = O.seq_meta(grids)
+        assert np.array_equal(cu, cu_o) and np.array_equal(pos, pos_o) and np.array_equal(perm, perm_o)
+
+
+def test_seq_meta_errors():
+    L = qv.lib()
+    cu = np.zeros(4, np.int32)
+    bad = np.array([[1, 3, 4]], np.int32)
+    assert L.qv_seq_meta(bad.ctypes.data, 1, 2, cu.ctypes.data, None, None) == _abi.QV_ERR_SHAPE
+    ok = np.array([[1, 4, 4]], np.int32)
+    assert L.qv_seq_meta(ok.ctypes.data, 1, 2, None, None, None) == _abi.QV_ERR_NULL
+    assert L.qv_seq_meta(ok.ctypes.data, 0, 2, cu.ctypes.data, None, None) == _abi.QV_ERR_SHAPE
+
+
+# Fake device addresses: every case below fails validation before any launch,
+# so they are never dereferenced.
+FAKE = ctypes.c_void_p(0x1000)
+
+
+def _vcfg(**kw):
+    d = dict(depth=1, dim=1280, heads=16, mlp=5120, patch_dim=1176, ld=1176, merge=2, dtype=_abi.QV_BF16,
+             ln_eps=1e-6, rope_theta=1e4)
+    d.update(kw)
+    return _abi.VisionCfg(**d)
+
+
+def _vforward(cfg, grids, ws_bytes=1 << 40, null_block=False):
+    L = qv.lib()
+    g = np.asarray(grids, np.int32).reshape(-1, 3)
+    blk = _abi.BlockW(*([0x2000] * 12))
+    if null_block:
+        blk.fc2_b = None
+    blocks = (_abi.BlockW * 1)(blk)
+    w = _abi.VisionW(0x3000, None, blocks)
+    return L.qv_vision_forward(ctypes.byref(cfg), ctypes.byref(w), FAKE, g.ctypes.data, len(g), FAKE, FAKE,
+                               ctypes.c_void_p(0x100000), ws_bytes, None)
+
+
+def test_vision_forward_validation():
+    L = qv.lib()
+    assert _vforward(_vcfg(), [(1, 3, 4)]) == _abi.QV_ERR_SHAPE
+    assert _vforward(_vcfg(dim=1000, heads=10), [(1, 4, 4)]) == _abi.QV_ERR_UNSUPPORTED
+    assert _vforward(_vcfg(heads=8), [(1, 4, 4)]) == _abi.QV_ERR_UNSUPPORTED
+    assert _vforward(_vcfg(mlp=5000), [(1, 4, 4)]) == _abi.QV_ERR_UNSUPPORTED
+    assert _vforward(_vcfg(ld=1170), [(1, 4, 4)]) == _abi.QV_ERR_SHAPE
+    assert _vforward(_vcfg(merge=3), [(1, 6, 6)]) == _abi.QV_ERR_UNSUPPORTED
+    assert _vforward(_vcfg(dtype=7), [(1, 4, 4)]) == _abi.QV_ERR_UNSUPPORTED
+    assert _vforward(_vcfg(), [(1, 4, 4)], ws_bytes=1024) == _abi.QV_ERR_WORKSPACE
+    assert _vforward(_vcfg(), [(1, 4, 4)], null_block=True) == _abi.QV_ERR_NULL
+    n = ctypes.c_size_t()
+    g = np.array([[1, 32, 32]], np.int32)
+    assert L.qv_vision_workspace_size(ctypes.byref(_vcfg()), g.ctypes.data, 1, ctypes.byref(n)) == 0
+    assert n.value > 1024 * 1280 * 2
+
+
+def test_patchify_validation():
+    L = qv.lib()
+    g = np.array([[1, 4, 4]], np.int32)
+    imgs = (_abi.Image * 1)(_abi.Image(0, 1, 3, 56, 57, 0))  # width not 14 * 4
+    assert L.qv_patchify(FAKE, imgs, 1, g.ctypes.data, None, FAKE, _abi.QV_BF16, 1176, None) == _abi.QV_ERR_SHAPE
+    imgs[0].width = 56
+    assert L.qv_patchify(FAKE, imgs, 1, g.ctypes.data, None, FAKE, _abi.QV_BF16, 1170, None) == _abi.QV_ERR_SHAPE
+    assert L.qv_patchify(None, imgs, 1, g.ctypes.data, None, FAKE, _abi.QV_BF16, 1176, None) == _abi.QV_ERR_NULL
+    imgs[0].frames = 3  # T must be ceil(3/2) = 2
+    assert L.qv_patchify(FAKE, imgs, 1, g.ctypes.data, None, FAKE, _abi.QV_BF16, 1176, None) == _abi.QV_ERR_SHAPE
+
+
+def test_merge_validation():
+    L = qv.lib()
+    w = _abi.MergerW(*([0x2000] * 6))
+    c = _abi.MergerCfg(1280, 2, 5120, 1536, _abi.QV_BF16, 1e-6)
+    args = lambda n, ws: (ctypes.byref(c), ctypes.byref(w), FAKE, n, FAKE, ctypes.c_void_p(0x100000), ws, None)
+    assert L.qv_patch_merge(*args(10, 1 << 40)) == _abi.QV_ERR_SHAPE
+    assert L.qv_patch_merge(*args(16, 16)) == _abi.QV_ERR_WORKSPACE
+    c.hidden = 5000
+    assert L.qv_patch_merge(*args(16, 1 << 40)) == _abi.QV_ERR_SHAPE
