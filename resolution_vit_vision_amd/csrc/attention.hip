@@ -9,8 +9,8 @@
 // prow0_i is a multiple of 128 and rows past an image's end are zero.
 // Output O is packed [N][ldo] with head h in columns 80h .. 80h+79.
 //
-// bf16 kernel (gfx950 MFMA, wave64): a workgroup owns 128 query rows of one
-// (image, head); each of its 4 waves owns 32.  Per 64-key tile a wave forms
+// bf16 kernel (gfx950 MFMA, wave64): each wave owns 32 query rows of one
+// (image, head) and a share of the keys.  Per 32-key block a wave forms
 // S^T = K . Q^T with v_mfma_f32_32x32x16_bf16 (5 k-steps over the 80 head
 // elements, so no padding), which leaves each lane holding one query column.
 // That register layout is directly the B operand of O^T = V^T . P^T, so P
@@ -40,29 +40,52 @@ __device__ __forceinline__ int find_plan(const PlanEntry* plan, int n_img, int g
   return lo;
 }
 
-constexpr int ABQ = 128;   // query rows per workgroup
-constexpr int ABK = 64;    // keys per tile
-constexpr int KSTR = 88;   // K tile row stride (elements): 176 B keeps 16-byte reads conflict-free
-constexpr int VSTR = 68;   // V^T tile row stride (elements)
+// Work split.  A workgroup is 4 waves = QW query groups x KW key groups.
+// Wave (qw, kw) owns query rows 32 qw .. 32 qw + 31 of the workgroup's tile
+// and, in every iteration, the kw-th sub-tile of KT keys of the KW * KT keys
+// staged in LDS.  With KW > 1 the partial (max, numerator, denominator) of
+// the KW key groups are combined through LDS at the end, so short images
+// still give the GPU enough workgroups.
+//
+// V^T keys are stored permuted inside each group of 16 (bits 2 and 3 of the
+// key index swapped, done by the q/k/v epilogue): the 8 keys one lane of the
+// P.V operand needs are then contiguous, one 16-byte LDS read.
+template <int KT>
+__device__ __forceinline__ int v_swz(int d, int chunk) {
+  return KT == 32 ? (chunk ^ ((d >> 2) & 3)) : (chunk ^ ((d >> 1) & 7));
+}
 
+template <int KW, int KT>
 __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a, float scale_log2) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][ABK * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][kHeadDim * VSTR];
+  constexpr int QW = 4 / KW;
+  constexpr int BQ = 32 * QW;
+  constexpr int IK = KW * KT;             // keys staged per iteration
+  constexpr int NCH = IK * kHeadDim / 8;  // 16-byte chunks of K (and of V^T) per iteration
+  constexpr int PER_T = (NCH + 255) / 256;
+  constexpr int SB = KT / 32;             // 32-key S^T blocks per wave sub-tile
+  // LDS: K rows of 80 elements, then V^T as [kw][80][KT]; reused for the combine
+  constexpr int K_ELEMS = IK * kHeadDim;
+  constexpr int V_ELEMS = KW * kHeadDim * KT;
+  constexpr int COMB_FLOATS = (KW > 1 ? (KW - 1) * QW * 49 * 64 : 1);
+  constexpr int LDS_BYTES = (2 * (K_ELEMS + V_ELEMS) > 4 * COMB_FLOATS) ? 2 * (K_ELEMS + V_ELEMS) : 4 * COMB_FLOATS;
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  uint16_t* sK = reinterpret_cast<uint16_t*>(lds);
+  uint16_t* sV = sK + K_ELEMS;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hlf = lane >> 5, l32 = lane & 31;
+  const int qw = wave / KW, kw = wave % KW;
   const int head = blockIdx.y;
   const int gt = blockIdx.x;
   const PlanEntry pe = a.plan[find_plan(a.plan, a.n_img, gt)];
   const int row0 = a.cu_seqlens[pe.img];
   const int n = a.cu_seqlens[pe.img + 1] - row0;
-  const int qbase = (gt - pe.qtile0) * ABQ + wave * 32;
+  const int qbase = (gt - pe.qtile0) * BQ + qw * 32;
 
   const uint16_t* Qh = reinterpret_cast<const uint16_t*>(a.q) + (size_t)head * a.P * kHeadDim;
   const uint16_t* Kh = reinterpret_cast<const uint16_t*>(a.k) + (size_t)head * a.P * kHeadDim;
   const uint16_t* Vh = reinterpret_cast<const uint16_t*>(a.vt) + (size_t)head * kHeadDim * a.P;
 
-  // B operand of S^T: lane holds query (qbase + l32), head elements 16kk + 8hlf .. +7
   bf16x8 qf[5];
   {
     const uint16_t* qr = Qh + (size_t)(pe.prow0 + qbase + l32) * kHeadDim + 8 * hlf;
@@ -70,31 +93,33 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a, float scale_log2)
     for (int kk = 0; kk < 5; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qr + 16 * kk);
   }
 
-  // tile staging: 640 16-byte chunks of K (64 rows x 10) and of V^T (80 rows x 8)
-  uint4 rk[3], rv[3];
-  auto gload = [&](int j) {
-    const int key0 = pe.prow0 + j * ABK;
+  uint4 rk[PER_T], rv[PER_T];
 #pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      const int id = tid + 256 * i;
-      if (id < 640) {
-        rk[i] = *reinterpret_cast<const uint4*>(Kh + (size_t)(key0 + id / 10) * kHeadDim + (id % 10) * 8);
-        rv[i] = *reinterpret_cast<const uint4*>(Vh + (size_t)(id >> 3) * a.P + key0 + (id & 7) * 8);
-      }
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      const int id = tid + 256 * i;
-      if (id < 640) {
-        *reinterpret_cast<uint4*>(&sK[buf][(id / 10) * KSTR + (id % 10) * 8]) = rk[i];
-        uint2* vp = reinterpret_cast<uint2*>(&sV[buf][(id >> 3) * VSTR + (id & 7) * 8]);
-        vp[0] = make_uint2(rv[i].x, rv[i].y);
-        vp[1] = make_uint2(rv[i].z, rv[i].w);
-      }
-    }
-  };
+  for (int i = 0; i < PER_T; ++i) rk[i] = rv[i] = make_uint4(0, 0, 0, 0);
+#define QV_ATTN_GLOAD(IT)                                                                                  \
+  {                                                                                                        \
+    const int key0 = pe.prow0 + (IT) * IK;                                                                 \
+    _Pragma("unroll") for (int i = 0; i < PER_T; ++i) {                                                    \
+      const int c = tid + 256 * i;                                                                         \
+      if (NCH % 256 == 0 || c < NCH) {                                                                     \
+        rk[i] = *reinterpret_cast<const uint4*>(Kh + (size_t)(key0 + c / 10) * kHeadDim + (c % 10) * 8);  \
+        const int d = c / (IK / 8), g = c % (IK / 8);                                                      \
+        rv[i] = *reinterpret_cast<const uint4*>(Vh + (size_t)d * a.P + key0 + g * 8);                      \
+      }                                                                                                    \
+    }                                                                                                      \
+  }
+#define QV_ATTN_SSTORE()                                                                                   \
+  {                                                                                                        \
+    _Pragma("unroll") for (int i = 0; i < PER_T; ++i) {                                                    \
+      const int c = tid + 256 * i;                                                                         \
+      if (NCH % 256 == 0 || c < NCH) {                                                                     \
+        *reinterpret_cast<uint4*>(&sK[(c / 10) * kHeadDim + (c % 10) * 8]) = rk[i];                        \
+        const int d = c / (IK / 8), g = c % (IK / 8);                                                      \
+        const int w = g / (KT / 8), cc = g % (KT / 8);                                                     \
+        *reinterpret_cast<uint4*>(&sV[(w * kHeadDim + d) * KT + (v_swz<KT>(d, cc) << 3)]) = rv[i];         \
+      }                                                                                                    \
+    }                                                                                                      \
+  }
 
   f32x16 o[3];
 #pragma unroll
@@ -103,7 +128,6 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a, float scale_log2)
     for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
   float m_run = -INFINITY;
 
-  // constant operand rows 80..95 of the padded V^T block: row 80 = 1, others 0
   bf16x8 vconst;
   {
     const __bf16 one = __builtin_bit_cast(__bf16, (uint16_t)(l32 == 16 ? 0x3F80 : 0));
@@ -111,38 +135,39 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a, float scale_log2)
     for (int e = 0; e < 8; ++e) vconst[e] = one;
   }
 
-  const int ntiles = (n + ABK - 1) / ABK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int j = 0; j < ntiles; ++j) {
-    const int cur = j & 1;
-    if (j + 1 < ntiles) gload(j + 1);
+  const int iters = (n + IK - 1) / IK;
+  QV_ATTN_GLOAD(0)
+  for (int it = 0; it < iters; ++it) {
+    __syncthreads();
+    QV_ATTN_SSTORE()
+    __syncthreads();
+    if (it + 1 < iters) QV_ATTN_GLOAD(it + 1)
+    const int kb = it * IK + kw * KT;  // first key of this wave's sub-tile
+    if (kb >= n) continue;             // wave-uniform: sub-tile entirely past the image
 
-    f32x16 s[2];
+    f32x16 s[SB];
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
+    for (int sb = 0; sb < SB; ++sb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[sb][r] = 0.f;
-      const uint16_t* kr = &sK[cur][(32 * sb + l32) * KSTR + 8 * hlf];
+      const uint16_t* kr = &sK[(kw * KT + 32 * sb + l32) * kHeadDim + 8 * hlf];
 #pragma unroll
       for (int kk = 0; kk < 5; ++kk)
         s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kr + 16 * kk), qf[kk],
                                                          s[sb], 0, 0, 0);
     }
-    // keys past the image end (last tile only) take no weight
-    if (j * ABK + ABK > n) {
+    if (kb + KT > n) {
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
+      for (int sb = 0; sb < SB; ++sb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = j * ABK + 32 * sb + 8 * (r >> 2) + 4 * hlf + (r & 3);
+          const int key = kb + 32 * sb + 8 * (r >> 2) + 4 * hlf + (r & 3);
           if (key >= n) s[sb][r] = -INFINITY;
         }
     }
     float mx = s[0][0];
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
+    for (int sb = 0; sb < SB; ++sb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
@@ -155,31 +180,63 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a, float scale_log2)
       for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
 
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
+    for (int sb = 0; sb < SB; ++sb)
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         bf16x8 pb;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           pb[e] = __builtin_bit_cast(__bf16, bf16_rne(exp2f(fmaf(s[sb][8 * s2 + e], scale_log2, -m_new))));
-        const int kofs = 32 * sb + 16 * s2 + 4 * hlf;
+        const int chunk = 4 * sb + 2 * s2 + hlf;
 #pragma unroll
         for (int t = 0; t < 3; ++t) {
           const int d = 32 * t + l32;
           bf16x8 vf;
-          if (t < 2 || l32 < kHeadDim - 64) {
-            const uint16_t* vp = &sV[cur][d * VSTR + kofs];
-            const uint2 lo = *reinterpret_cast<const uint2*>(vp);
-            const uint2 hi = *reinterpret_cast<const uint2*>(vp + 8);
-            vf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-          } else {
+          if (t < 2 || l32 < kHeadDim - 64)
+            vf = *reinterpret_cast<const bf16x8*>(&sV[(kw * kHeadDim + d) * KT + (v_swz<KT>(d, chunk) << 3)]);
+          else
             vf = vconst;
-          }
           o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, o[t], 0, 0, 0);
         }
       }
-    if (j + 1 < ntiles) sstore(cur ^ 1);
+  }
+
+  if constexpr (KW > 1) {
+    // combine the KW key groups of each query group: O = sum_w 2^(m_w - M) O_w
+    float* comb = reinterpret_cast<float*>(lds);
     __syncthreads();
+    if (kw > 0) {
+      float* dst = comb + ((kw - 1) * QW + qw) * 49 * 64;
+#pragma unroll
+      for (int t = 0; t < 3; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dst[(t * 16 + r) * 64 + lane] = o[t][r];
+      dst[48 * 64 + lane] = m_run;
+    }
+    __syncthreads();
+    if (kw > 0) return;
+    float mw[KW];
+    mw[0] = m_run;
+    float M = m_run;
+#pragma unroll
+    for (int w = 1; w < KW; ++w) {
+      mw[w] = comb[((w - 1) * QW + qw) * 49 * 64 + 48 * 64 + lane];
+      M = fmaxf(M, mw[w]);
+    }
+    const float s0 = exp2f(mw[0] - M);
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[t][r] *= s0;
+#pragma unroll
+    for (int w = 1; w < KW; ++w) {
+      const float sw = exp2f(mw[w] - M);
+      const float* src = comb + ((w - 1) * QW + qw) * 49 * 64;
+#pragma unroll
+      for (int t = 0; t < 3; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[t][r] = fmaf(src[(t * 16 + r) * 64 + lane], sw, o[t][r]);
+    }
   }
 
   // O^T row 80 (block 2, local row 16) = register 8 of the lower half-wave
@@ -201,12 +258,28 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a, float scale_log2)
         }
       }
   }
+#undef QV_ATTN_GLOAD
+#undef QV_ATTN_SSTORE
+}
+
+int attention_bf16_rows_per_wg(int64_t wgs_at_128) {
+  // enough workgroups for two per CU: split keys across waves when the
+  // 128-row tiling leaves the GPU under-filled
+  if (wgs_at_128 >= 512) return 128;
+  if (wgs_at_128 * 2 >= 512) return 64;
+  return 32;
 }
 
 hipError_t attention_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.total_qtiles == 0) return hipSuccess;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)kHeadDim);
-  hipLaunchKernelGGL(k_attn_bf16, dim3((unsigned)a.total_qtiles, (unsigned)a.heads), dim3(256), 0, s, a, scale_log2);
+  const dim3 grid((unsigned)a.total_qtiles, (unsigned)a.heads);
+  switch (a.rows_per_wg) {
+    case 128: hipLaunchKernelGGL((k_attn_bf16<1, 64>), grid, dim3(256), 0, s, a, scale_log2); break;
+    case 64: hipLaunchKernelGGL((k_attn_bf16<2, 32>), grid, dim3(256), 0, s, a, scale_log2); break;
+    case 32: hipLaunchKernelGGL((k_attn_bf16<4, 32>), grid, dim3(256), 0, s, a, scale_log2); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -3,18 +3,15 @@
 //
 // A is [M][lda] (activations), B is [N][ldb] (a Linear weight, [out][in]);
 // both are K-contiguous, so one 16-byte global load moves 8 consecutive k of
-// one row.  Tiles of BK = 64 are staged through LDS with an XOR swizzle of
-// the 16-byte chunks (chunk ^ (row & 7)) so that the per-lane 16-byte reads of
-// the v_mfma_f32_32x32x16_bf16 operand pattern (32 rows, two k-chunks) spread
-// over all banks.  Global loads for tile k+1 are issued before the MFMAs of
-// tile k and written to the other LDS buffer after them (one barrier per
-// tile).
+// one row.  The tower's K (1280 and 5120) runs on the multi-stage
+// direct-to-LDS kernel of gemm_pipe.h; any other K (the 1176-wide patch
+// embedding) on a register-staged kernel below that handles K tails: tiles of
+// BK = 64 go through registers into a double-buffered LDS tile with the same
+// chunk swizzle, loads for tile k+1 issued before the MFMAs of tile k.
+#include "gemm_pipe.h"
 #include "qv_internal.h"
 
 namespace qv {
-
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ uint16_t bf16_bits(float f) {
   uint32_t u = __builtin_bit_cast(uint32_t, f);
@@ -103,7 +100,8 @@ struct EpiActBf16 {
 // B-row loader applies the same map, so both halves of a pair land in the
 // same lane (MFMA blocks fn and fn + 1) and the rotation needs no exchange.
 // The v third is stored transposed per head ([head][80][P]) for the
-// attention kernel's P.V product.
+// attention kernel's P.V product, with the keys of every aligned group of 16
+// permuted by swapping bits 2 and 3 of the key index.
 __device__ __forceinline__ int qkv_weight_row(int v, int dim) {
   if (v >= 2 * dim) return v;
   const int region = v >= dim ? 1 : 0;
@@ -169,7 +167,12 @@ struct EpiQkv {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int row = QV_ACC_ROW(wm0, fm, r, lane);
-            if (row < M) dst[o.tokinfo[row].y] = bf16_bits(acc[fm][fn][r] + bb);
+            if (row < M) {
+              // keys permuted inside each group of 16 (bits 2 and 3 swapped) for the attention kernel
+              const int pr = o.tokinfo[row].y;
+              const int pp = (pr & ~12) | ((pr & 4) << 1) | ((pr & 8) >> 1);
+              dst[pp] = bf16_bits(acc[fm][fn][r] + bb);
+            }
           }
       }
     }
@@ -206,7 +209,7 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(const uint16_t* __restrict__ 
     aok[i] = g < M;
     ap[i] = A + (size_t)(aok[i] ? g : 0) * lda + c * 8;
     akc[i] = c * 8;
-    aoff[i] = r * BK + ((c ^ (r & 7)) << 3);
+    aoff[i] = r * BK + (swz_chunk(r, c) << 3);
   }
   const uint16_t* bp[BCH];
   int boff[BCH], bkc[BCH];
@@ -218,7 +221,7 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(const uint16_t* __restrict__ 
     bok[i] = g < N;
     bp[i] = B + (size_t)rmap(bok[i] ? g : 0) * ldb + c * 8;
     bkc[i] = c * 8;
-    boff[i] = r * BK + ((c ^ (r & 7)) << 3);
+    boff[i] = r * BK + (swz_chunk(r, c) << 3);
   }
 
   uint4 ra[ACH], rb[BCH];
@@ -260,12 +263,12 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(const uint16_t* __restrict__ 
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) {
         const int r = arow + fm * 32;
-        a[fm] = *reinterpret_cast<const bf16x8*>(&sA[cur][r * BK + ((c ^ (r & 7)) << 3)]);
+        a[fm] = *reinterpret_cast<const bf16x8*>(&sA[cur][r * BK + (swz_chunk(r, c) << 3)]);
       }
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
         const int r = brow + fn * 32;
-        b[fn] = *reinterpret_cast<const bf16x8*>(&sB[cur][r * BK + ((c ^ (r & 7)) << 3)]);
+        b[fn] = *reinterpret_cast<const bf16x8*>(&sB[cur][r * BK + (swz_chunk(r, c) << 3)]);
       }
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
@@ -279,10 +282,38 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(const uint16_t* __restrict__ 
   epi.apply(acc, m0 + wm * TM, n0 + wn * TN, lane, M, N);
 }
 
+template <int BM, int BN, int WM, int WN, int ST, int KT, class Epi, class RowMap>
+static hipError_t launch_pipe(const void* A, int lda, const void* B, int ldb, int M, int N, const Epi& epi,
+                              RowMap rmap, hipStream_t s) {
+  const unsigned tiles = (unsigned)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
+  const int raster = M <= 2048 ? 0 : 1;
+  hipLaunchKernelGGL((k_gemm_pipe<BM, BN, WM, WN, ST, KT, Epi, RowMap>), dim3(tiles), dim3(WM * WN * 64), 0, s,
+                     reinterpret_cast<const uint16_t*>(A), lda, reinterpret_cast<const uint16_t*>(B), ldb, M, N,
+                     raster, 8, epi, rmap);
+  return hipGetLastError();
+}
+
+// Tile shape by how many output tiles the problem has: 256x256 (8 waves) when
+// that already fills the GPU, 128x128 (8 waves) for mid sizes, 64x128 when N
+// is narrow and M small (the 448x448 image's N = 1280 projections).
+template <int KT, class Epi, class RowMap>
+static hipError_t run_pipe(const void* A, int lda, const void* B, int ldb, int M, int N, const Epi& epi,
+                           RowMap rmap, hipStream_t s) {
+  const int64_t t256 = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t t128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
+  if (t256 >= 256) return launch_pipe<256, 256, 2, 4, 2, KT>(A, lda, B, ldb, M, N, epi, rmap, s);
+  if (t128 >= 200) return launch_pipe<128, 128, 4, 2, 3, KT>(A, lda, B, ldb, M, N, epi, rmap, s);
+  return launch_pipe<64, 128, 2, 2, 4, KT>(A, lda, B, ldb, M, N, epi, rmap, s);
+}
+
 template <class Epi, class RowMap>
 static hipError_t run_bf16(const void* A, int lda, const void* B, int ldb, int M, int N, int K, const Epi& epi,
                            RowMap rmap, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
+  const bool aligned = (lda % 8 == 0) && (ldb % 8 == 0);
+  if (aligned && K == 1280) return run_pipe<20>(A, lda, B, ldb, M, N, epi, rmap, s);
+  if (aligned && K == 5120) return run_pipe<80>(A, lda, B, ldb, M, N, epi, rmap, s);
+  // any other K (the 1176-wide patch embedding): register-staged kernel with K tails
   constexpr int BM = 128, BN = 128;
   const unsigned tiles = (unsigned)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
   hipLaunchKernelGGL((k_gemm_bf16<BM, BN, 2, 2, Epi, RowMap>), dim3(tiles), dim3(256), 0, s,
@@ -293,7 +324,13 @@ static hipError_t run_bf16(const void* A, int lda, const void* B, int ldb, int M
 
 hipError_t gemm_bf16_store_f32(const void* A, int lda, const void* B, int ldb, int M, int N, int K,
                                const float* bias, float* C, int ldc, hipStream_t s) {
-  return run_bf16(A, lda, B, ldb, M, N, K, EpiStoreF32{C, ldc, bias}, RowMapIdentity{}, s);
+  if (M <= 0 || N <= 0) return hipSuccess;
+  constexpr int BM = 128, BN = 128;
+  const unsigned tiles = (unsigned)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
+  hipLaunchKernelGGL((k_gemm_bf16<BM, BN, 2, 2, EpiStoreF32, RowMapIdentity>), dim3(tiles), dim3(256), 0, s,
+                     reinterpret_cast<const uint16_t*>(A), lda, reinterpret_cast<const uint16_t*>(B), ldb, M, N, K,
+                     EpiStoreF32{C, ldc, bias}, RowMapIdentity{});
+  return hipGetLastError();
 }
 hipError_t gemm_bf16_resid_f32(const void* A, int lda, const void* B, int ldb, int M, int N, int K,
                                const float* bias, float* Z, int ldz, hipStream_t s) {

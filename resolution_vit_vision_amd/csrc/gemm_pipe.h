@@ -1,0 +1,239 @@
+// Multi-stage C = A . B^T for gfx950 with direct global->LDS loads.
+//
+// Each stage holds a BM x 64 tile of A and a BN x 64 tile of B (bf16, row =
+// 128 bytes of 8 16-byte chunks).  Tiles are fetched with
+// global_load_lds_dwordx4: one instruction moves 64 lanes x 16 bytes into 1 KB
+// of LDS at the wave-uniform base (lane l lands at base + 16 l), so the LDS
+// layout is chosen by which global chunk each lane fetches.  The layout is
+// row-major with the chunk index XOR-ed by (row >> 1) & 7: the operand reads
+// of v_mfma_f32_32x32x16_bf16 (32 consecutive rows, one 16-byte chunk per
+// lane, two chunks per wave) then hit 64 distinct banks per 16 lanes.
+//
+// STAGES buffers form a ring; loads for tile kt + STAGES - 1 are issued
+// right after the barrier that opens tile kt, so STAGES - 1 tiles are in
+// flight while one is consumed.  The waits are explicit vmcnt counts (each
+// wave waits for its own loads of the tile, then the barrier publishes all
+// waves' loads); the ring uses one __shared__ array per stage and a
+// statically unrolled loop so that every LDS access names its stage.
+#pragma once
+
+#include "qv_internal.h"
+
+namespace qv {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef const __attribute__((address_space(1))) void* gas_ptr;
+typedef __attribute__((address_space(3))) void* las_ptr;
+
+// s_waitcnt with vmcnt <= n and no constraint on the other counters (gfx9 encoding).
+#define QV_WAIT_VM(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 0xF) | 0x70 | 0xF00 | ((((n) >> 4) & 3) << 14))
+// Workgroup barrier without the memory fence __syncthreads() implies (which
+// would wait for every load in flight); compiler-level ordering is kept.
+#define QV_BARRIER()                      \
+  do {                                    \
+    asm volatile("" ::: "memory");        \
+    __builtin_amdgcn_s_barrier();         \
+    asm volatile("" ::: "memory");        \
+  } while (0)
+
+__device__ __forceinline__ int swz_chunk(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+
+template <int BM_, int BN_, int WM, int WN, int STAGES>
+struct PipeCfg {
+  static constexpr int BM = BM_, BN = BN_;
+  static constexpr int NW = WM * WN;
+  static constexpr int NT = NW * 64;
+  static constexpr int BK = 64;
+  static constexpr int TM = BM_ / WM, TN = BN_ / WN;
+  static constexpr int FM = TM / 32, FN = TN / 32;
+  static constexpr int STAGE_ELEMS = (BM_ + BN_) * BK;        // bf16 elements per stage
+  static constexpr int LOADS_A = BM_ * 8 / NT;                // 16-byte chunks per thread per stage
+  static constexpr int LOADS_B = BN_ * 8 / NT;
+  static constexpr int LOADS = LOADS_A + LOADS_B;             // vmcnt of one stage per wave
+  static_assert(FM >= 1 && FN >= 1, "wave tile at least 32x32");
+  static_assert(BM_ * 8 % NT == 0 && BN_ * 8 % NT == 0, "whole 1 KB chunks per wave");
+  static_assert(STAGES >= 2 && STAGES <= 8, "2..8 stages");
+};
+
+template <class C>
+struct PipeState {
+  const char* gsrc[C::LOADS];   // per-thread global address of its chunk at k = 0
+  uint32_t ldst[C::LOADS];      // wave-uniform LDS byte offset of the 1 KB block inside a stage
+};
+
+template <class C, class RowMap>
+__device__ __forceinline__ void pipe_setup(PipeState<C>& ps, const uint16_t* A, int lda, const uint16_t* B, int ldb,
+                                           int M, int N, int m0, int n0, RowMap rmap, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < C::LOADS; ++i) {
+    // 1 KB block index inside the stage: A blocks first, then B blocks
+    const int blk = i * C::NW + wave;
+    const int p = blk * 64 + lane;        // 16-byte slot inside the stage
+    const bool isA = p < C::BM * 8;
+    const int q = isA ? p : p - C::BM * 8;
+    const int r = q >> 3;                 // tile row
+    const int c = swz_chunk(r, q & 7);    // logical k chunk stored at this slot
+    if (isA) {
+      int g = m0 + r;
+      g = g < M ? g : M - 1;
+      ps.gsrc[i] = reinterpret_cast<const char*>(A + (size_t)g * lda + c * 8);
+    } else {
+      int g = n0 + r;
+      g = g < N ? g : N - 1;
+      ps.gsrc[i] = reinterpret_cast<const char*>(B + (size_t)rmap(g) * ldb + c * 8);
+    }
+    ps.ldst[i] = (uint32_t)(blk * 1024);
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void pipe_issue(const PipeState<C>& ps, uint16_t* stage, int kt) {
+#pragma unroll
+  for (int i = 0; i < C::LOADS; ++i)
+    __builtin_amdgcn_global_load_lds((gas_ptr)(ps.gsrc[i] + (size_t)kt * 128),
+                                     (las_ptr)(reinterpret_cast<char*>(stage) + ps.ldst[i]), 16, 0, 0);
+}
+
+// Operand fragments are software-pipelined: the LDS reads of k-step kk + 1
+// are issued before the MFMAs of k-step kk (the scheduler is fenced so it
+// cannot hoist the MFMAs above them), so LDS latency overlaps matrix work.
+template <class C>
+__device__ __forceinline__ void pipe_read(const uint16_t* stage, bf16x8 (&a)[C::FM], bf16x8 (&b)[C::FN], int kk,
+                                          int arow, int brow, int lane) {
+  const uint16_t* sA = stage;
+  const uint16_t* sB = stage + C::BM * C::BK;
+  const int c = kk * 2 + (lane >> 5);
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm) {
+    const int r = arow + fm * 32;
+    a[fm] = *reinterpret_cast<const bf16x8*>(&sA[r * C::BK + (swz_chunk(r, c) << 3)]);
+  }
+#pragma unroll
+  for (int fn = 0; fn < C::FN; ++fn) {
+    const int r = brow + fn * 32;
+    b[fn] = *reinterpret_cast<const bf16x8*>(&sB[r * C::BK + (swz_chunk(r, c) << 3)]);
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void pipe_compute(const uint16_t* stage, f32x16 (&acc)[C::FM][C::FN], int wm, int wn,
+                                             int lane) {
+  const int arow = wm * C::TM + (lane & 31), brow = wn * C::TN + (lane & 31);
+  constexpr int KS = C::BK / 16;
+  bf16x8 a[2][C::FM], b[2][C::FN];
+  pipe_read<C>(stage, a[0], b[0], 0, arow, brow, lane);
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    if (kk + 1 < KS) pipe_read<C>(stage, a[(kk + 1) & 1], b[(kk + 1) & 1], kk + 1, arow, brow, lane);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk & 1][fm], b[kk & 1][fn], acc[fm][fn], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Tile order.  Workgroups are dispatched round-robin over the 8 XCDs
+// (workgroup b runs on XCD b % 8), and each XCD has its own L2.  `raster`
+// selects how the tile grid is cut between XCDs:
+//   raster 0: XCD x owns a contiguous band of column tiles (all row tiles),
+//             so each weight panel is fetched into exactly one L2 and the
+//             (small) activation matrix is replicated: right when M is small;
+//   raster 1: XCD x owns a contiguous band of row tiles, and inside the band
+//             tiles are visited in groups of `group` row tiles sweeping the
+//             column tiles, so the weight panels in flight are shared by
+//             `group` concurrent row tiles: right when M is large.
+__device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int raster, int group, int& tm,
+                                            int& tn) {
+  const int total = tiles_m * tiles_n;
+  if (raster == 0) {
+    if (tiles_n % 8 == 0) {
+      const int per_x = tiles_n / 8;            // column tiles per XCD
+      const int x = bid % 8, i = bid / 8;       // i-th workgroup of XCD x
+      tm = i % tiles_m;
+      tn = x * per_x + i / tiles_m;
+    } else {
+      tm = bid % tiles_m;
+      tn = bid / tiles_m;
+    }
+    return;
+  }
+  int t = bid;
+  if (total % 8 == 0) t = (bid % 8) * (total / 8) + bid / 8;
+  // grouped order over the linear index t
+  const int per_group = group * tiles_n;
+  const int g = t / per_group, first_m = g * group;
+  const int gm = (tiles_m - first_m) < group ? (tiles_m - first_m) : group;
+  const int r = t % per_group;
+  tm = first_m + r % gm;
+  tn = r / gm;
+}
+
+// Statically unrolled K loop: with no loop-carried merge point the compiler
+// knows exactly which stage each LDS-DMA wrote, so the only waits are the
+// explicit per-tile vmcnt counts.
+template <class C, int KT, int STAGES>
+struct PipeSteps {
+  template <int kt>
+  static __device__ __forceinline__ void run(uint16_t* const (&st)[8], const PipeState<C>& ps,
+                                             f32x16 (&acc)[C::FM][C::FN], int wm, int wn, int lane) {
+    if constexpr (kt < KT) {
+      constexpr int later = (KT - 1 - kt) < (STAGES - 2) ? (KT - 1 - kt) : (STAGES - 2);
+      QV_WAIT_VM(later * C::LOADS);
+      QV_BARRIER();
+      if constexpr (kt + STAGES - 1 < KT) pipe_issue<C>(ps, st[(kt + STAGES - 1) % STAGES], kt + STAGES - 1);
+      pipe_compute<C>(st[kt % STAGES], acc, wm, wn, lane);
+      run<kt + 1>(st, ps, acc, wm, wn, lane);
+    }
+  }
+};
+
+// KT = K / 64 is a compile-time constant (the tower's K is 1280 or 5120).
+template <int BM, int BN, int WM, int WN, int STAGES, int KT, class Epi, class RowMap>
+__global__ __launch_bounds__(WM * WN * 64) void k_gemm_pipe(const uint16_t* __restrict__ A, int lda,
+                                                            const uint16_t* __restrict__ B, int ldb, int M, int N,
+                                                            int raster, int group, Epi epi, RowMap rmap) {
+  using C = PipeCfg<BM, BN, WM, WN, STAGES>;
+  constexpr int SE = C::STAGE_ELEMS;
+  __shared__ __attribute__((aligned(1024))) uint16_t st0[SE];
+  __shared__ __attribute__((aligned(1024))) uint16_t st1[SE];
+  __shared__ __attribute__((aligned(1024))) uint16_t st2[STAGES > 2 ? SE : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t st3[STAGES > 3 ? SE : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t st4[STAGES > 4 ? SE : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t st5[STAGES > 5 ? SE : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t st6[STAGES > 6 ? SE : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t st7[STAGES > 7 ? SE : 8];
+  uint16_t* const st[8] = {st0, st1, st2, st3, st4, st5, st6, st7};
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int tiles_n = (N + BN - 1) / BN, tiles_m = (M + BM - 1) / BM;
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m, tiles_n, raster, group, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  PipeState<C> ps;
+  pipe_setup<C>(ps, A, lda, B, ldb, M, N, m0, n0, rmap, wave, lane);
+
+  f32x16 acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // prologue: STAGES - 1 tiles in flight
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < KT) pipe_issue<C>(ps, st[s], s);
+  PipeSteps<C, KT, STAGES>::template run<0>(st, ps, acc, wm, wn, lane);
+  epi.apply(acc, m0 + wm * C::TM, n0 + wn * C::TN, lane, M, N);
+}
+
+}  // namespace qv

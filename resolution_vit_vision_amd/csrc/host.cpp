@@ -233,6 +233,7 @@ struct VisionPlan {
   int n_img = 0;
   int max_pos = 0;
   int total_qtiles = 0;
+  int attn_rows = 0;  // query rows per attention workgroup
   bool padded = false;
   size_t es = 2;
   std::vector<ImgDesc> desc;
@@ -270,7 +271,6 @@ qv_status make_plan(const qv_vision_cfg* c, const int32_t* grid_thw, int32_t n_i
   vp.n_img = n_img;
   vp.N = total;
   vp.es = c->dtype == QV_BF16 ? 2 : 4;
-  const int bq = c->dtype == QV_BF16 ? kAttnBQ_bf16 : kAttnBQ_f32;
   vp.desc.resize(n_img);
   int64_t row = 0, prow = 0;
   for (int i = 0; i < n_img; ++i) {
@@ -284,6 +284,10 @@ qv_status make_plan(const qv_vision_cfg* c, const int32_t* grid_thw, int32_t n_i
   }
   vp.P = prow;
   if (vp.P > INT32_MAX / 2) return fail(QV_ERR_SHAPE, "batch too large");
+  int64_t tiles128 = 0;
+  for (int i = 0; i < n_img; ++i) tiles128 += (vp.desc[i].n + 127) / 128;
+  vp.attn_rows = c->dtype == QV_BF16 ? attention_bf16_rows_per_wg(tiles128 * c->heads) : kAttnBQ_f32;
+  const int bq = vp.attn_rows;
   // attention work plan: longest images first so the tail of the grid is short
   std::vector<int> order(n_img);
   for (int i = 0; i < n_img; ++i) order[i] = i;
@@ -394,7 +398,7 @@ qv_status qv_vision_forward(const qv_vision_cfg* c, const qv_vision_w* w, const 
     QV_LAUNCH(QV_KC_PATCH_EMBED, s, gemm_f32_store(reinterpret_cast<const float*>(patches), c->ld, reinterpret_cast<const float*>(w->patch_w),
                           c->patch_dim, M, D, c->patch_dim, reinterpret_cast<const float*>(w->patch_b), hidden, D, s));
 
-  AttnArgs aa{qo.q, qo.k, qo.vt, O, D, cu_seqlens, plan, n_img, (int)vp.P, c->heads, vp.total_qtiles};
+  AttnArgs aa{qo.q, qo.k, qo.vt, O, D, cu_seqlens, plan, n_img, (int)vp.P, c->heads, vp.total_qtiles, vp.attn_rows};
   for (int l = 0; l < c->depth; ++l) {
     const qv_block_w& b = w->blocks[l];
     QV_LAUNCH(QV_KC_LAYERNORM, s, launch_layernorm(hidden, (const float*)b.ln1_w, (const float*)b.ln1_b, A, bf, M, D, c->ln_eps, s));

@@ -104,10 +104,11 @@ struct AttnArgs {
   int P;
   int heads;
   int total_qtiles;
+  int rows_per_wg;   // query rows per workgroup of the bf16 kernel (128, 64 or 32)
 };
 hipError_t attention_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t attention_f32(const AttnArgs& a, hipStream_t s);
-constexpr int kAttnBQ_bf16 = 128;
+int attention_bf16_rows_per_wg(int64_t wgs_at_128);
 constexpr int kAttnBQ_f32 = 64;
 
 }  // namespace qv
