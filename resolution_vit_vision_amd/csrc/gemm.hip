@@ -8,6 +8,8 @@
 // embedding) on a register-staged kernel below that handles K tails: tiles of
 // BK = 64 go through registers into a double-buffered LDS tile with the same
 // chunk swizzle, loads for tile k+1 issued before the MFMAs of tile k.
+#include <type_traits>
+
 #include "gemm_pipe.h"
 #include "qv_internal.h"
 
@@ -30,35 +32,93 @@ __device__ __forceinline__ float act_apply(Act a, float u) {
 #define QV_ACC_COL(wn0, fn, lane) ((wn0) + (fn) * 32 + ((lane) & 31))
 
 // ------------------------------------------------------------- epilogues
+// Staged epilogue: each 32x32 MFMA block of a wave goes through a private
+// 32 x 40-float LDS patch (row pitch 40 floats: the two half-waves' rows land
+// 32 banks apart, and rows stay 16-byte aligned), then is read back so that
+// a lane owns VEC consecutive columns of one row and writes them with one
+// 16-byte (f32 x 4) or 8/16-byte (bf16) store.  Scattered 4-byte stores
+// straight from the MFMA layout measured 4-8 B/clk per CU.
+// pre(col, v): value to stage (bias, activation); store(row, col, v[VEC]).
+template <int VEC, class Op, int FM, int FN>
+__device__ __forceinline__ void staged_store(const Op& op, f32x16 (&acc)[FM][FN], float* wlds, int wm0, int wn0,
+                                             int lane, int M, int N) {
+  constexpr int LD = 40;
+  constexpr int LPR = 32 / VEC;          // lanes per 32-column row
+  constexpr int RPP = 64 / LPR;          // rows per pass
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      const int col0 = wn0 + fn * 32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rl = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        wlds[rl * LD + (lane & 31)] = op.pre(col0 + (lane & 31), acc[fm][fn][r]);
+      }
+#pragma unroll
+      for (int pass = 0; pass < 32 / RPP; ++pass) {
+        const int rl = pass * RPP + lane / LPR;
+        const int cl = (lane % LPR) * VEC;
+        float v[VEC];
+#pragma unroll
+        for (int q = 0; q < VEC; q += 4) {
+          const float4 t = *reinterpret_cast<const float4*>(&wlds[rl * LD + cl + q]);
+          v[q] = t.x; v[q + 1] = t.y; v[q + 2] = t.z; v[q + 3] = t.w;
+        }
+        const int row = wm0 + fm * 32 + rl, col = col0 + cl;
+        if (row < M && col < N) op.store(row, col, v);
+      }
+    }
+}
+
 struct EpiStoreF32 {
+  static constexpr bool kStaged = true;
   float* C; int ldc; const float* bias;
+  __device__ float pre(int col, float v) const { return v + (bias ? bias[col] : 0.f); }
+  __device__ void store(int row, int col, const float (&v)[4]) const {
+    *reinterpret_cast<float4*>(C + (size_t)row * ldc + col) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+  template <int FM, int FN>
+  __device__ void apply_staged(f32x16 (&acc)[FM][FN], float* wlds, int wm0, int wn0, int lane, int M, int N) const {
+    staged_store<4>(*this, acc, wlds, wm0, wn0, lane, M, N);
+  }
   template <int FM, int FN>
   __device__ void apply(f32x16 (&acc)[FM][FN], int wm0, int wn0, int lane, int M, int N) const {
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
       const int col = QV_ACC_COL(wn0, fn, lane);
       if (col >= N) continue;
-      const float bb = bias ? bias[col] : 0.f;
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = QV_ACC_ROW(wm0, fm, r, lane);
-          if (row < M) C[(size_t)row * ldc + col] = acc[fm][fn][r] + bb;
+          if (row < M) C[(size_t)row * ldc + col] = pre(col, acc[fm][fn][r]);
         }
     }
   }
 };
 
 struct EpiResidF32 {
+  static constexpr bool kStaged = true;
   float* Z; int ldz; const float* bias;
+  __device__ float pre(int col, float v) const { return v + bias[col]; }
+  __device__ void store(int row, int col, const float (&v)[4]) const {
+    float4* p = reinterpret_cast<float4*>(Z + (size_t)row * ldz + col);
+    float4 z = *p;
+    z.x += v[0]; z.y += v[1]; z.z += v[2]; z.w += v[3];
+    *p = z;
+  }
+  template <int FM, int FN>
+  __device__ void apply_staged(f32x16 (&acc)[FM][FN], float* wlds, int wm0, int wn0, int lane, int M, int N) const {
+    staged_store<4>(*this, acc, wlds, wm0, wn0, lane, M, N);
+  }
   template <int FM, int FN>
   __device__ void apply(f32x16 (&acc)[FM][FN], int wm0, int wn0, int lane, int M, int N) const {
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
       const int col = QV_ACC_COL(wn0, fn, lane);
       if (col >= N) continue;
-      const float bb = bias[col];
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -66,7 +126,7 @@ struct EpiResidF32 {
           const int row = QV_ACC_ROW(wm0, fm, r, lane);
           if (row < M) {
             float* p = Z + (size_t)row * ldz + col;
-            *p = *p + (acc[fm][fn][r] + bb);
+            *p = *p + pre(col, acc[fm][fn][r]);
           }
         }
     }
@@ -74,20 +134,33 @@ struct EpiResidF32 {
 };
 
 struct EpiActBf16 {
+  static constexpr bool kStaged = true;
   uint16_t* C; int ldc; const float* bias; Act act;
+  __device__ float pre(int col, float v) const { return act_apply(act, v + bias[col]); }
+  __device__ void store(int row, int col, const float (&v)[8]) const {
+    uint4 pk;
+    pk.x = bf16_bits(v[0]) | ((uint32_t)bf16_bits(v[1]) << 16);
+    pk.y = bf16_bits(v[2]) | ((uint32_t)bf16_bits(v[3]) << 16);
+    pk.z = bf16_bits(v[4]) | ((uint32_t)bf16_bits(v[5]) << 16);
+    pk.w = bf16_bits(v[6]) | ((uint32_t)bf16_bits(v[7]) << 16);
+    *reinterpret_cast<uint4*>(C + (size_t)row * ldc + col) = pk;
+  }
+  template <int FM, int FN>
+  __device__ void apply_staged(f32x16 (&acc)[FM][FN], float* wlds, int wm0, int wn0, int lane, int M, int N) const {
+    staged_store<8>(*this, acc, wlds, wm0, wn0, lane, M, N);
+  }
   template <int FM, int FN>
   __device__ void apply(f32x16 (&acc)[FM][FN], int wm0, int wn0, int lane, int M, int N) const {
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
       const int col = QV_ACC_COL(wn0, fn, lane);
       if (col >= N) continue;
-      const float bb = bias[col];
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = QV_ACC_ROW(wm0, fm, r, lane);
-          if (row < M) C[(size_t)row * ldc + col] = bf16_bits(act_apply(act, acc[fm][fn][r] + bb));
+          if (row < M) C[(size_t)row * ldc + col] = bf16_bits(pre(col, acc[fm][fn][r]));
         }
     }
   }
@@ -121,6 +194,7 @@ struct RowMapQkv {
 };
 
 struct EpiQkv {
+  static constexpr bool kStaged = false;
   QkvOut o; const float* bias;
   template <int FM, int FN>
   __device__ void apply(f32x16 (&acc)[FM][FN], int wm0, int wn0, int lane, int M, int N) const {
@@ -294,15 +368,22 @@ static hipError_t launch_pipe(const void* A, int lda, const void* B, int ldb, in
 }
 
 // Tile shape by how many output tiles the problem has: 256x256 (8 waves) when
-// that already fills the GPU, 128x128 (8 waves) for mid sizes, 64x128 when N
-// is narrow and M small (the 448x448 image's N = 1280 projections).
-template <int KT, class Epi, class RowMap>
+// that already fills the GPU; 128x160 (4 waves of 32x160) when N is a
+// multiple of 160 and that tiling fills one wave of 256 workgroups (the
+// 448x448 image's MLP up-projection: 8 x 32 tiles); 128x128 (8 waves) for
+// other mid sizes; 64x128 when N is narrow and M small.  The q/k/v epilogue
+// needs wave tiles whose width is a multiple of 64, which 32x160 is not.
+template <int KT, bool ALLOW160, class Epi, class RowMap>
 static hipError_t run_pipe(const void* A, int lda, const void* B, int ldb, int M, int N, const Epi& epi,
                            RowMap rmap, hipStream_t s) {
   const int64_t t256 = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
   const int64_t t128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
+  const int64_t t160 = (int64_t)((M + 127) / 128) * (N / 160);
   if (t256 >= 256) return launch_pipe<256, 256, 2, 4, 2, KT>(A, lda, B, ldb, M, N, epi, rmap, s);
-  if (t128 >= 200) return launch_pipe<128, 128, 4, 2, 3, KT>(A, lda, B, ldb, M, N, epi, rmap, s);
+  if constexpr (ALLOW160)
+    if (N % 160 == 0 && t160 >= 192 && t160 <= 256)
+      return launch_pipe<128, 160, 4, 1, 4, KT>(A, lda, B, ldb, M, N, epi, rmap, s);
+  if (t128 >= 200) return launch_pipe<128, 128, 4, 2, 4, KT>(A, lda, B, ldb, M, N, epi, rmap, s);
   return launch_pipe<64, 128, 2, 2, 4, KT>(A, lda, B, ldb, M, N, epi, rmap, s);
 }
 
@@ -310,9 +391,12 @@ template <class Epi, class RowMap>
 static hipError_t run_bf16(const void* A, int lda, const void* B, int ldb, int M, int N, int K, const Epi& epi,
                            RowMap rmap, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
-  const bool aligned = (lda % 8 == 0) && (ldb % 8 == 0);
-  if (aligned && K == 1280) return run_pipe<20>(A, lda, B, ldb, M, N, epi, rmap, s);
-  if (aligned && K == 5120) return run_pipe<80>(A, lda, B, ldb, M, N, epi, rmap, s);
+  // 16-byte rows for the LDS-DMA loads; whole 32-column groups for the staged 16-byte stores
+  const bool aligned = (lda % 8 == 0) && (ldb % 8 == 0) && (N % 32 == 0);
+  constexpr bool is_qkv = std::is_same<Epi, EpiQkv>::value;  // always K = dim = 1280
+  if (aligned && K == 1280) return run_pipe<20, !is_qkv>(A, lda, B, ldb, M, N, epi, rmap, s);
+  if constexpr (!is_qkv)
+    if (aligned && K == 5120) return run_pipe<80, true>(A, lda, B, ldb, M, N, epi, rmap, s);
   // any other K (the 1176-wide patch embedding): register-staged kernel with K tails
   constexpr int BM = 128, BN = 128;
   const unsigned tiles = (unsigned)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));

@@ -233,7 +233,16 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_pipe(const uint16_t* __re
   for (int s = 0; s < STAGES - 1; ++s)
     if (s < KT) pipe_issue<C>(ps, st[s], s);
   PipeSteps<C, KT, STAGES>::template run<0>(st, ps, acc, wm, wn, lane);
-  epi.apply(acc, m0 + wm * C::TM, n0 + wn * C::TN, lane, M, N);
+  if constexpr (Epi::kStaged) {
+    // every wave is done reading the ring: reuse it as per-wave staging
+    // patches of 32 x 40 floats (waves 0-3 in stage 0, waves 4-7 in stage 1)
+    static_assert(4 * 32 * 40 * 4 <= C::STAGE_ELEMS * 2, "staging patches fit in one stage");
+    QV_BARRIER();
+    float* wl = reinterpret_cast<float*>(wave < 4 ? st0 : st1) + (wave & 3) * (32 * 40);
+    epi.apply_staged(acc, wl, m0 + wm * C::TM, n0 + wn * C::TN, lane, M, N);
+  } else {
+    epi.apply(acc, m0 + wm * C::TM, n0 + wn * C::TN, lane, M, N);
+  }
 }
 
 }  // namespace qv
