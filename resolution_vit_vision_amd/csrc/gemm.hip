@@ -73,6 +73,7 @@ __device__ __forceinline__ void staged_store(const Op& op, f32x16 (&acc)[FM][FN]
 
 struct EpiStoreF32 {
   static constexpr bool kStaged = true;
+  static constexpr int kPatchFloats = 32 * 40;
   float* C; int ldc; const float* bias;
   __device__ float pre(int col, float v) const { return v + (bias ? bias[col] : 0.f); }
   __device__ void store(int row, int col, const float (&v)[4]) const {
@@ -101,6 +102,7 @@ struct EpiStoreF32 {
 
 struct EpiResidF32 {
   static constexpr bool kStaged = true;
+  static constexpr int kPatchFloats = 32 * 40;
   float* Z; int ldz; const float* bias;
   __device__ float pre(int col, float v) const { return v + bias[col]; }
   __device__ void store(int row, int col, const float (&v)[4]) const {
@@ -135,6 +137,7 @@ struct EpiResidF32 {
 
 struct EpiActBf16 {
   static constexpr bool kStaged = true;
+  static constexpr int kPatchFloats = 32 * 40;
   uint16_t* C; int ldc; const float* bias; Act act;
   __device__ float pre(int col, float v) const { return act_apply(act, v + bias[col]); }
   __device__ void store(int row, int col, const float (&v)[8]) const {
@@ -194,13 +197,113 @@ struct RowMapQkv {
 };
 
 struct EpiQkv {
-  static constexpr bool kStaged = false;
+  static constexpr bool kStaged = true;
+  static constexpr int kPatchFloats = 32 * 72;  // q/k: 32 rows x (64 + 8) floats
   QkvOut o; const float* bias;
+
+  // Staged: rotated q/k values of a 32-row block go to LDS as [row][half*32 + c]
+  // and leave as 16-byte runs of 8 consecutive head elements (an aligned run
+  // of 8 pairs never crosses a head, heads being 40 pairs); v goes to LDS
+  // transposed [feature][row] and leaves as 8-byte runs of 4 consecutive keys
+  // (a 4-aligned run of packed rows stays inside one image and maps to 4
+  // contiguous key slots even after the bits-2/3 key permutation).
+  template <int FM, int FN>
+  __device__ void apply_staged(f32x16 (&acc)[FM][FN], float* wlds, int wm0, int wn0, int lane, int M, int N) const {
+    const int dim = o.dim;
+    const int c = lane & 31;
+    if (wn0 < 2 * dim) {
+#pragma unroll
+      for (int fp = 0; fp < FN; fp += 2) {
+        const int v0 = wn0 + fp * 32;  // first virtual column of this 64-group
+        const int region = v0 >= dim ? 1 : 0;
+        const int g = (v0 - region * dim) >> 6;
+        const int pair = 32 * g + c;
+        const int head = pair / (kHeadDim / 2), j = pair % (kHeadDim / 2);
+        const int f0 = region * dim + head * kHeadDim + j;
+        const float b0 = bias[f0], b1 = bias[f0 + kHeadDim / 2];
+        const int fi = j < kRopeFreqs ? j : j - kRopeFreqs;
+        uint16_t* base = reinterpret_cast<uint16_t*>(region ? o.k : o.q);
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+          const int rb = wm0 + fm * 32;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int rl = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            const int row = rb + rl;
+            float y0 = 0.f, y1 = 0.f;
+            if (row < M) {
+              const int2 ti = o.tokinfo[row];
+              const int p = j < kRopeFreqs ? (ti.x & 0xFFFF) : (ti.x >> 16);
+              const float2 cs = o.rope[p * kRopeFreqs + fi];
+              const float x0 = acc[fm][fp][r] + b0, x1 = acc[fm][fp + 1][r] + b1;
+              y0 = x0 * cs.x - x1 * cs.y;
+              y1 = x1 * cs.x + x0 * cs.y;
+            }
+            wlds[rl * 72 + c] = y0;
+            wlds[rl * 72 + 32 + c] = y1;
+          }
+#pragma unroll
+          for (int pass = 0; pass < 4; ++pass) {
+            const int task = pass * 64 + lane;
+            const int rl = task >> 3, h = (task >> 2) & 1, q = task & 3;
+            const int row = rb + rl;
+            const float4 a0 = *reinterpret_cast<const float4*>(&wlds[rl * 72 + 32 * h + 8 * q]);
+            const float4 a1 = *reinterpret_cast<const float4*>(&wlds[rl * 72 + 32 * h + 8 * q + 4]);
+            if (row < M) {
+              const int p0 = 32 * g + 8 * q;
+              const int hd = p0 / (kHeadDim / 2), j0 = p0 % (kHeadDim / 2);
+              uint4 pk;
+              pk.x = bf16_bits(a0.x) | ((uint32_t)bf16_bits(a0.y) << 16);
+              pk.y = bf16_bits(a0.z) | ((uint32_t)bf16_bits(a0.w) << 16);
+              pk.z = bf16_bits(a1.x) | ((uint32_t)bf16_bits(a1.y) << 16);
+              pk.w = bf16_bits(a1.z) | ((uint32_t)bf16_bits(a1.w) << 16);
+              const size_t off = ((size_t)hd * o.P + o.tokinfo[row].y) * kHeadDim + j0 + h * (kHeadDim / 2);
+              *reinterpret_cast<uint4*>(base + off) = pk;
+            }
+          }
+        }
+      }
+    } else {
+      uint16_t* vt = reinterpret_cast<uint16_t*>(o.vt);
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int col0 = wn0 + fn * 32;
+        const float bb = bias[col0 + c];
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+          const int rb = wm0 + fm * 32;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int rl = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            wlds[c * 36 + rl] = acc[fm][fn][r] + bb;
+          }
+#pragma unroll
+          for (int pass = 0; pass < 4; ++pass) {
+            const int task = pass * 64 + lane;
+            const int cf = task >> 3, g4 = task & 7;
+            const int row = rb + 4 * g4;
+            const float4 a = *reinterpret_cast<const float4*>(&wlds[cf * 36 + 4 * g4]);
+            if (row < M) {
+              const int f = col0 + cf - 2 * dim;
+              const int hd = f / kHeadDim, dd = f % kHeadDim;
+              const int pr = o.tokinfo[row].y;
+              const int pp = (pr & ~12) | ((pr & 4) << 1) | ((pr & 8) >> 1);
+              uint2 pk;
+              pk.x = bf16_bits(a.x) | ((uint32_t)bf16_bits(a.y) << 16);
+              pk.y = bf16_bits(a.z) | ((uint32_t)bf16_bits(a.w) << 16);
+              *reinterpret_cast<uint2*>(vt + ((size_t)hd * kHeadDim + dd) * o.P + pp) = pk;
+            }
+          }
+        }
+      }
+    }
+  }
+  // Direct (unstaged) form for the register-staged kernel, used when the
+  // width is not one the pipelined kernel is instantiated for.
   template <int FM, int FN>
   __device__ void apply(f32x16 (&acc)[FM][FN], int wm0, int wn0, int lane, int M, int N) const {
     const int dim = o.dim;
     if (wn0 < 2 * dim) {
-      // the wave's columns are whole 64-groups of the q or k third
 #pragma unroll
       for (int fp = 0; fp < FN; fp += 2) {
         const int v = QV_ACC_COL(wn0, fp, lane);
@@ -242,7 +345,6 @@ struct EpiQkv {
           for (int r = 0; r < 16; ++r) {
             const int row = QV_ACC_ROW(wm0, fm, r, lane);
             if (row < M) {
-              // keys permuted inside each group of 16 (bits 2 and 3 swapped) for the attention kernel
               const int pr = o.tokinfo[row].y;
               const int pp = (pr & ~12) | ((pr & 4) << 1) | ((pr & 8) >> 1);
               dst[pp] = bf16_bits(acc[fm][fn][r] + bb);

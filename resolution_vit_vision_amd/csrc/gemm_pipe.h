@@ -234,11 +234,15 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_pipe(const uint16_t* __re
     if (s < KT) pipe_issue<C>(ps, st[s], s);
   PipeSteps<C, KT, STAGES>::template run<0>(st, ps, acc, wm, wn, lane);
   if constexpr (Epi::kStaged) {
-    // every wave is done reading the ring: reuse it as per-wave staging
-    // patches of 32 x 40 floats (waves 0-3 in stage 0, waves 4-7 in stage 1)
-    static_assert(4 * 32 * 40 * 4 <= C::STAGE_ELEMS * 2, "staging patches fit in one stage");
+    // every wave is done reading the ring: reuse it as one private staging
+    // patch per wave (PER patches per stage buffer)
+    constexpr int PER = (C::STAGE_ELEMS * 2) / (Epi::kPatchFloats * 4);
+    static_assert(PER >= 1 && PER * STAGES >= C::NW, "staging patches fit in the ring");
     QV_BARRIER();
-    float* wl = reinterpret_cast<float*>(wave < 4 ? st0 : st1) + (wave & 3) * (32 * 40);
+    const int sb = wave / PER;  // select without indexing the pointer table (no static address table)
+    uint16_t* sbuf = sb == 0 ? st0 : sb == 1 ? st1 : sb == 2 ? st2 : sb == 3 ? st3 : sb == 4 ? st4 : sb == 5 ? st5
+                   : sb == 6 ? st6 : st7;
+    float* wl = reinterpret_cast<float*>(sbuf) + (wave % PER) * Epi::kPatchFloats;
     epi.apply_staged(acc, wl, m0 + wm * C::TM, n0 + wn * C::TN, lane, M, N);
   } else {
     epi.apply(acc, m0 + wm * C::TM, n0 + wn * C::TN, lane, M, N);
