@@ -16,6 +16,9 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqv.so")
 SOURCES = ["host.cpp", "misc.hip", "gemm.hip", "attention.hip"]
+# The attention kernel rescales and reads its MFMA accumulators every key
+# block; keeping them in arch VGPRs avoids AGPR<->VGPR copies on each use.
+EXTRA_FLAGS = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 
@@ -39,7 +42,7 @@ def build(verbose: bool = False) -> str:
     def compile_one(src):
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [cc, *common_flags(), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *common_flags(), *EXTRA_FLAGS.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         out = (r.stdout + r.stderr).replace(
             "'-packed-fp32-ops' is not a recognized feature for this target (ignoring feature)\n", "")

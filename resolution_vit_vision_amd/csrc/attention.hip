@@ -25,11 +25,20 @@ namespace qv {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-__device__ __forceinline__ uint16_t bf16_rne(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats to packed bf16, round to nearest even (one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
+
+// The running reference of the online softmax only moves when a score
+// exceeds it by more than 2^kLazyLog2 (scores in log2 units).  Numerator and
+// denominator share the reference, so the result does not depend on it; the
+// rescale of the 48 O accumulators then happens once or twice per row
+// instead of every key block, and P stays <= 2^kLazyLog2 (safe in bf16/f32).
+constexpr float kLazyLog2 = 8.0f;
 
 __device__ __forceinline__ int find_plan(const PlanEntry* plan, int n_img, int gt) {
   int lo = 0, hi = n_img - 1;
@@ -75,8 +84,21 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a, float scale_log2)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hlf = lane >> 5, l32 = lane & 31;
   const int qw = wave / KW, kw = wave % KW;
-  const int head = blockIdx.y;
-  const int gt = blockIdx.x;
+  // Flat grid over (head, q-tile).  Workgroup b runs on XCD b % 8; when the
+  // heads divide evenly, XCD x gets heads [x*H/8, (x+1)*H/8) so each L2 keeps
+  // the K and V of only its own heads.
+  int head, gt;
+  {
+    const int b = blockIdx.x, T = a.total_qtiles;
+    if (a.heads % 8 == 0) {
+      const int hpx = a.heads / 8, local = b / 8;
+      head = (b % 8) * hpx + local / T;
+      gt = local % T;
+    } else {
+      head = b / T;
+      gt = b % T;
+    }
+  }
   const PlanEntry pe = a.plan[find_plan(a.plan, a.n_img, gt)];
   const int row0 = a.cu_seqlens[pe.img];
   const int n = a.cu_seqlens[pe.img + 1] - row0;
@@ -171,13 +193,17 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a, float scale_log2)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx * scale_log2);
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
+    const float cand = mx * scale_log2;
+    const bool grow = cand > m_run + kLazyLog2;  // first block: m_run = -inf
+    if (__any(grow)) {
+      const float m_new = grow ? cand : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first block, 1 where kept
+      m_run = m_new;
 #pragma unroll
-    for (int t = 0; t < 3; ++t)
+      for (int t = 0; t < 3; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+        for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+    }
 
 #pragma unroll
     for (int sb = 0; sb < SB; ++sb)
@@ -186,7 +212,7 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a, float scale_log2)
         bf16x8 pb;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          pb[e] = __builtin_bit_cast(__bf16, bf16_rne(exp2f(fmaf(s[sb][8 * s2 + e], scale_log2, -m_new))));
+          pb[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[sb][8 * s2 + e], scale_log2, -m_run));
         const int chunk = 4 * sb + 2 * s2 + hlf;
 #pragma unroll
         for (int t = 0; t < 3; ++t) {
@@ -223,14 +249,14 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a, float scale_log2)
       mw[w] = comb[((w - 1) * QW + qw) * 49 * 64 + 48 * 64 + lane];
       M = fmaxf(M, mw[w]);
     }
-    const float s0 = exp2f(mw[0] - M);
+    const float s0 = __builtin_amdgcn_exp2f(mw[0] - M);
 #pragma unroll
     for (int t = 0; t < 3; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[t][r] *= s0;
 #pragma unroll
     for (int w = 1; w < KW; ++w) {
-      const float sw = exp2f(mw[w] - M);
+      const float sw = __builtin_amdgcn_exp2f(mw[w] - M);
       const float* src = comb + ((w - 1) * QW + qw) * 49 * 64;
 #pragma unroll
       for (int t = 0; t < 3; ++t)
@@ -252,8 +278,8 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a, float scale_log2)
         const int d0 = 32 * t + 8 * g + 4 * hlf;
         if (d0 < kHeadDim) {
           uint2 pk;
-          pk.x = bf16_rne(o[t][4 * g] * inv) | ((uint32_t)bf16_rne(o[t][4 * g + 1] * inv) << 16);
-          pk.y = bf16_rne(o[t][4 * g + 2] * inv) | ((uint32_t)bf16_rne(o[t][4 * g + 3] * inv) << 16);
+          pk.x = pack_bf16(o[t][4 * g] * inv, o[t][4 * g + 1] * inv);
+          pk.y = pack_bf16(o[t][4 * g + 2] * inv, o[t][4 * g + 3] * inv);
           *reinterpret_cast<uint2*>(orow + d0) = pk;
         }
       }
@@ -273,7 +299,7 @@ int attention_bf16_rows_per_wg(int64_t wgs_at_128) {
 hipError_t attention_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.total_qtiles == 0) return hipSuccess;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)kHeadDim);
-  const dim3 grid((unsigned)a.total_qtiles, (unsigned)a.heads);
+  const dim3 grid((unsigned)a.total_qtiles * (unsigned)a.heads);
   switch (a.rows_per_wg) {
     case 128: hipLaunchKernelGGL((k_attn_bf16<1, 64>), grid, dim3(256), 0, s, a, scale_log2); break;
     case 64: hipLaunchKernelGGL((k_attn_bf16<2, 32>), grid, dim3(256), 0, s, a, scale_log2); break;

@@ -458,12 +458,12 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(const uint16_t* __restrict__ 
   epi.apply(acc, m0 + wm * TM, n0 + wn * TN, lane, M, N);
 }
 
-template <int BM, int BN, int WM, int WN, int ST, int KT, class Epi, class RowMap>
+template <int BM, int BN, int WM, int WN, int ST, int KT, int KS = 1, class Epi, class RowMap>
 static hipError_t launch_pipe(const void* A, int lda, const void* B, int ldb, int M, int N, const Epi& epi,
                               RowMap rmap, hipStream_t s) {
   const unsigned tiles = (unsigned)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
   const int raster = M <= 2048 ? 0 : 1;
-  hipLaunchKernelGGL((k_gemm_pipe<BM, BN, WM, WN, ST, KT, Epi, RowMap>), dim3(tiles), dim3(WM * WN * 64), 0, s,
+  hipLaunchKernelGGL((k_gemm_pipe<BM, BN, WM, WN, ST, KT / KS, KS, Epi, RowMap>), dim3(tiles), dim3(WM * WN * KS * 64), 0, s,
                      reinterpret_cast<const uint16_t*>(A), lda, reinterpret_cast<const uint16_t*>(B), ldb, M, N,
                      raster, 8, epi, rmap);
   return hipGetLastError();
@@ -486,7 +486,8 @@ static hipError_t run_pipe(const void* A, int lda, const void* B, int ldb, int M
     if (N % 160 == 0 && t160 >= 192 && t160 <= 256)
       return launch_pipe<128, 160, 4, 1, 4, KT>(A, lda, B, ldb, M, N, epi, rmap, s);
   if (t128 >= 200) return launch_pipe<128, 128, 4, 2, 4, KT>(A, lda, B, ldb, M, N, epi, rmap, s);
-  return launch_pipe<64, 128, 2, 2, 4, KT>(A, lda, B, ldb, M, N, epi, rmap, s);
+  // few tiles: two wave groups split K inside each workgroup
+  return launch_pipe<64, 128, 2, 2, 3, KT, 2>(A, lda, B, ldb, M, N, epi, rmap, s);
 }
 
 template <class Epi, class RowMap>

@@ -40,26 +40,34 @@ typedef __attribute__((address_space(3))) void* las_ptr;
 
 __device__ __forceinline__ int swz_chunk(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
-template <int BM_, int BN_, int WM, int WN, int STAGES>
+// KS wave groups of WM x WN waves share one LDS ring; every pipeline step
+// stages KS consecutive 64-deep k-tiles and group g multiplies the g-th one,
+// so each group walks half of K when KS = 2 (the partial sums are added
+// through LDS at the end).  This doubles the waves per workgroup (and halves
+// the serial K loop) when the output alone gives too few workgroups.
+template <int BM_, int BN_, int WM, int WN, int STAGES, int KS_ = 1>
 struct PipeCfg {
-  static constexpr int BM = BM_, BN = BN_;
-  static constexpr int NW = WM * WN;
+  static constexpr int BM = BM_, BN = BN_, KS = KS_;
+  static constexpr int NWG = WM * WN;                         // waves per group
+  static constexpr int NW = NWG * KS_;
   static constexpr int NT = NW * 64;
   static constexpr int BK = 64;
   static constexpr int TM = BM_ / WM, TN = BN_ / WN;
   static constexpr int FM = TM / 32, FN = TN / 32;
-  static constexpr int STAGE_ELEMS = (BM_ + BN_) * BK;        // bf16 elements per stage
-  static constexpr int LOADS_A = BM_ * 8 / NT;                // 16-byte chunks per thread per stage
-  static constexpr int LOADS_B = BN_ * 8 / NT;
+  static constexpr int SUB_ELEMS = (BM_ + BN_) * BK;          // one 64-deep k-tile of A and B
+  static constexpr int STAGE_ELEMS = SUB_ELEMS * KS_;         // bf16 elements per stage
+  static constexpr int LOADS_A = BM_ * 8 * KS_ / NT;          // 16-byte chunks per thread per stage
+  static constexpr int LOADS_B = BN_ * 8 * KS_ / NT;
   static constexpr int LOADS = LOADS_A + LOADS_B;             // vmcnt of one stage per wave
   static_assert(FM >= 1 && FN >= 1, "wave tile at least 32x32");
-  static_assert(BM_ * 8 % NT == 0 && BN_ * 8 % NT == 0, "whole 1 KB chunks per wave");
+  static_assert(BM_ * 8 % (NWG * 64) == 0 && BN_ * 8 % (NWG * 64) == 0, "whole 1 KB chunks per wave");
   static_assert(STAGES >= 2 && STAGES <= 8, "2..8 stages");
+  static_assert(KS_ == 1 || KS_ == 2, "K split 1 or 2");
 };
 
 template <class C>
 struct PipeState {
-  const char* gsrc[C::LOADS];   // per-thread global address of its chunk at k = 0
+  const char* gsrc[C::LOADS];   // per-thread global address of its chunk at step 0
   uint32_t ldst[C::LOADS];      // wave-uniform LDS byte offset of the 1 KB block inside a stage
 };
 
@@ -68,21 +76,23 @@ __device__ __forceinline__ void pipe_setup(PipeState<C>& ps, const uint16_t* A, 
                                            int M, int N, int m0, int n0, RowMap rmap, int wave, int lane) {
 #pragma unroll
   for (int i = 0; i < C::LOADS; ++i) {
-    // 1 KB block index inside the stage: A blocks first, then B blocks
+    // 1 KB block index inside the stage: per k sub-tile, A blocks first, then B blocks
     const int blk = i * C::NW + wave;
-    const int p = blk * 64 + lane;        // 16-byte slot inside the stage
-    const bool isA = p < C::BM * 8;
-    const int q = isA ? p : p - C::BM * 8;
-    const int r = q >> 3;                 // tile row
-    const int c = swz_chunk(r, q & 7);    // logical k chunk stored at this slot
+    const int p = blk * 64 + lane;              // 16-byte slot inside the stage
+    const int ks = p / ((C::BM + C::BN) * 8);   // k sub-tile
+    const int pq = p % ((C::BM + C::BN) * 8);
+    const bool isA = pq < C::BM * 8;
+    const int q = isA ? pq : pq - C::BM * 8;
+    const int r = q >> 3;                       // tile row
+    const int c = swz_chunk(r, q & 7);          // logical k chunk stored at this slot
     if (isA) {
       int g = m0 + r;
       g = g < M ? g : M - 1;
-      ps.gsrc[i] = reinterpret_cast<const char*>(A + (size_t)g * lda + c * 8);
+      ps.gsrc[i] = reinterpret_cast<const char*>(A + (size_t)g * lda + ks * 64 + c * 8);
     } else {
       int g = n0 + r;
       g = g < N ? g : N - 1;
-      ps.gsrc[i] = reinterpret_cast<const char*>(B + (size_t)rmap(g) * ldb + c * 8);
+      ps.gsrc[i] = reinterpret_cast<const char*>(B + (size_t)rmap(g) * ldb + ks * 64 + c * 8);
     }
     ps.ldst[i] = (uint32_t)(blk * 1024);
   }
@@ -92,7 +102,7 @@ template <class C>
 __device__ __forceinline__ void pipe_issue(const PipeState<C>& ps, uint16_t* stage, int kt) {
 #pragma unroll
   for (int i = 0; i < C::LOADS; ++i)
-    __builtin_amdgcn_global_load_lds((gas_ptr)(ps.gsrc[i] + (size_t)kt * 128),
+    __builtin_amdgcn_global_load_lds((gas_ptr)(ps.gsrc[i] + (size_t)kt * 128 * C::KS),
                                      (las_ptr)(reinterpret_cast<char*>(stage) + ps.ldst[i]), 16, 0, 0);
 }
 
@@ -180,24 +190,25 @@ template <class C, int KT, int STAGES>
 struct PipeSteps {
   template <int kt>
   static __device__ __forceinline__ void run(uint16_t* const (&st)[8], const PipeState<C>& ps,
-                                             f32x16 (&acc)[C::FM][C::FN], int wm, int wn, int lane) {
+                                             f32x16 (&acc)[C::FM][C::FN], int wm, int wn, int lane, int sub) {
     if constexpr (kt < KT) {
       constexpr int later = (KT - 1 - kt) < (STAGES - 2) ? (KT - 1 - kt) : (STAGES - 2);
       QV_WAIT_VM(later * C::LOADS);
       QV_BARRIER();
       if constexpr (kt + STAGES - 1 < KT) pipe_issue<C>(ps, st[(kt + STAGES - 1) % STAGES], kt + STAGES - 1);
-      pipe_compute<C>(st[kt % STAGES], acc, wm, wn, lane);
-      run<kt + 1>(st, ps, acc, wm, wn, lane);
+      pipe_compute<C>(st[kt % STAGES] + sub, acc, wm, wn, lane);
+      run<kt + 1>(st, ps, acc, wm, wn, lane, sub);
     }
   }
 };
 
-// KT = K / 64 is a compile-time constant (the tower's K is 1280 or 5120).
-template <int BM, int BN, int WM, int WN, int STAGES, int KT, class Epi, class RowMap>
-__global__ __launch_bounds__(WM * WN * 64) void k_gemm_pipe(const uint16_t* __restrict__ A, int lda,
-                                                            const uint16_t* __restrict__ B, int ldb, int M, int N,
-                                                            int raster, int group, Epi epi, RowMap rmap) {
-  using C = PipeCfg<BM, BN, WM, WN, STAGES>;
+// KT = (K / 64) / KS pipeline steps is a compile-time constant (the tower's K
+// is 1280 or 5120).
+template <int BM, int BN, int WM, int WN, int STAGES, int KT, int KS, class Epi, class RowMap>
+__global__ __launch_bounds__(WM * WN * KS * 64) void k_gemm_pipe(const uint16_t* __restrict__ A, int lda,
+                                                                 const uint16_t* __restrict__ B, int ldb, int M,
+                                                                 int N, int raster, int group, Epi epi, RowMap rmap) {
+  using C = PipeCfg<BM, BN, WM, WN, STAGES, KS>;
   constexpr int SE = C::STAGE_ELEMS;
   __shared__ __attribute__((aligned(1024))) uint16_t st0[SE];
   __shared__ __attribute__((aligned(1024))) uint16_t st1[SE];
@@ -211,7 +222,8 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_pipe(const uint16_t* __re
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / WN, wn = wave % WN;
+  const int kgrp = wave / C::NWG, wig = wave % C::NWG;  // k group, wave inside the group
+  const int wm = wig / WN, wn = wig % WN;
   const int tiles_n = (N + BN - 1) / BN, tiles_m = (M + BM - 1) / BM;
   int tm, tn;
   tile_coords(blockIdx.x, tiles_m, tiles_n, raster, group, tm, tn);
@@ -228,22 +240,44 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_pipe(const uint16_t* __re
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // prologue: STAGES - 1 tiles in flight
+  // prologue: STAGES - 1 steps in flight
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
     if (s < KT) pipe_issue<C>(ps, st[s], s);
-  PipeSteps<C, KT, STAGES>::template run<0>(st, ps, acc, wm, wn, lane);
-  if constexpr (Epi::kStaged) {
-    // every wave is done reading the ring: reuse it as one private staging
-    // patch per wave (PER patches per stage buffer)
-    constexpr int PER = (C::STAGE_ELEMS * 2) / (Epi::kPatchFloats * 4);
-    static_assert(PER >= 1 && PER * STAGES >= C::NW, "staging patches fit in the ring");
+  PipeSteps<C, KT, STAGES>::template run<0>(st, ps, acc, wm, wn, lane, kgrp * C::SUB_ELEMS);
+
+  constexpr int ACC_FLOATS = KS == 2 ? C::FM * C::FN * 16 * 64 : 0;  // one wave's accumulators
+  constexpr int SLOT = ACC_FLOATS > Epi::kPatchFloats ? ACC_FLOATS : Epi::kPatchFloats;
+  // every wave is done reading the ring: reuse stage 0 (and 1) as one slot per
+  // wave of the first group, for the k-group reduction and then the staged
+  // epilogue patch of that wave
+  constexpr int PER = (SE * 2) / (SLOT * 4);
+  static_assert(PER >= 1 && PER * STAGES >= C::NWG, "per-wave slots fit in the ring");
+  QV_BARRIER();
+  const int sb = wig / PER;
+  uint16_t* sbuf = sb == 0 ? st0 : sb == 1 ? st1 : sb == 2 ? st2 : sb == 3 ? st3 : sb == 4 ? st4 : sb == 5 ? st5
+                 : sb == 6 ? st6 : st7;
+  float* slot = reinterpret_cast<float*>(sbuf) + (wig % PER) * SLOT;
+  if constexpr (KS == 2) {
+    if (kgrp == 1) {
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) slot[((i * C::FN + j) * 16 + r) * 64 + lane] = acc[i][j][r];
+    }
     QV_BARRIER();
-    const int sb = wave / PER;  // select without indexing the pointer table (no static address table)
-    uint16_t* sbuf = sb == 0 ? st0 : sb == 1 ? st1 : sb == 2 ? st2 : sb == 3 ? st3 : sb == 4 ? st4 : sb == 5 ? st5
-                   : sb == 6 ? st6 : st7;
-    float* wl = reinterpret_cast<float*>(sbuf) + (wave % PER) * Epi::kPatchFloats;
-    epi.apply_staged(acc, wl, m0 + wm * C::TM, n0 + wn * C::TN, lane, M, N);
+    if (kgrp == 1) return;
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] += slot[((i * C::FN + j) * 16 + r) * 64 + lane];
+  }
+  if constexpr (Epi::kStaged) {
+    epi.apply_staged(acc, slot, m0 + wm * C::TM, n0 + wn * C::TN, lane, M, N);
   } else {
     epi.apply(acc, m0 + wm * C::TM, n0 + wn * C::TN, lane, M, N);
   }
