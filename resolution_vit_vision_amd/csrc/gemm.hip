@@ -15,10 +15,13 @@
 
 namespace qv {
 
-__device__ __forceinline__ uint16_t bf16_bits(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// float -> bf16 bits, round to nearest even (hardware v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint16_t bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ float act_apply(Act a, float u) {
@@ -38,27 +41,69 @@ __device__ __forceinline__ float act_apply(Act a, float u) {
 // a lane owns VEC consecutive columns of one row and writes them with one
 // 16-byte (f32 x 4) or 8/16-byte (bf16) store.  Scattered 4-byte stores
 // straight from the MFMA layout measured 4-8 B/clk per CU.
-// pre(col, v): value to stage (bias, activation); store(row, col, v[VEC]).
+//
+// Every global load of the epilogue (bias, residual) is issued before its
+// first store.  On gfx9 the vector-memory counter covers stores as well as
+// loads and completes in order, so a load issued after a store makes the
+// wave wait for that store's write acknowledgement, a round trip that cost
+// microseconds per 32x32 block when all workgroups store at once.
+// Op interface: col_param(col) (per-column value, e.g. bias), pre(cp, v)
+// (value to stage), row_param(row, col) (per-store value loaded up front,
+// e.g. the residual) and store(row, col, v[VEC], rp).
+struct NoRowParam {};
+
 template <int VEC, class Op, int FM, int FN>
 __device__ __forceinline__ void staged_store(const Op& op, f32x16 (&acc)[FM][FN], float* wlds, int wm0, int wn0,
                                              int lane, int M, int N) {
   constexpr int LD = 40;
   constexpr int LPR = 32 / VEC;          // lanes per 32-column row
   constexpr int RPP = 64 / LPR;          // rows per pass
+  constexpr int PASSES = 32 / RPP;
+  using RP = typename Op::RowParam;
+  float cp[FN];
 #pragma unroll
-  for (int fm = 0; fm < FM; ++fm)
+  for (int fn = 0; fn < FN; ++fn) {
+    const int col = wn0 + fn * 32 + (lane & 31);
+    cp[fn] = col < N ? op.col_param(col) : 0.f;
+  }
+  const int rl0 = lane / LPR, cl = (lane % LPR) * VEC;
+  // residual-style row params: all of them up front when they fit in 64
+  // registers, otherwise one 32-row block at a time
+  constexpr bool ALL = FM * FN * PASSES * Op::kRowParamFloats <= 64;
+  RP rp[ALL ? FM : 1][FN][PASSES];
+  if constexpr (Op::kRowParamFloats > 0 && ALL) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int pass = 0; pass < PASSES; ++pass) {
+          const int row = wm0 + fm * 32 + pass * RPP + rl0, col = wn0 + fn * 32 + cl;
+          if (row < M && col < N) rp[fm][fn][pass] = op.row_param(row, col);
+        }
+  }
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+    if constexpr (Op::kRowParamFloats > 0 && !ALL) {
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int pass = 0; pass < PASSES; ++pass) {
+          const int row = wm0 + fm * 32 + pass * RPP + rl0, col = wn0 + fn * 32 + cl;
+          if (row < M && col < N) rp[0][fn][pass] = op.row_param(row, col);
+        }
+    }
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
       const int col0 = wn0 + fn * 32;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int rl = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        wlds[rl * LD + (lane & 31)] = op.pre(col0 + (lane & 31), acc[fm][fn][r]);
+        wlds[rl * LD + (lane & 31)] = op.pre(cp[fn], acc[fm][fn][r]);
       }
 #pragma unroll
-      for (int pass = 0; pass < 32 / RPP; ++pass) {
-        const int rl = pass * RPP + lane / LPR;
-        const int cl = (lane % LPR) * VEC;
+      for (int pass = 0; pass < PASSES; ++pass) {
+        const int rl = pass * RPP + rl0;
         float v[VEC];
 #pragma unroll
         for (int q = 0; q < VEC; q += 4) {
@@ -66,17 +111,29 @@ __device__ __forceinline__ void staged_store(const Op& op, f32x16 (&acc)[FM][FN]
           v[q] = t.x; v[q + 1] = t.y; v[q + 2] = t.z; v[q + 3] = t.w;
         }
         const int row = wm0 + fm * 32 + rl, col = col0 + cl;
-        if (row < M && col < N) op.store(row, col, v);
+        if (row < M && col < N) op.store(row, col, v, rp[ALL ? fm : 0][fn][pass]);
       }
     }
+  }
+}
+
+// QuickGELU for the bf16 path with a hardware reciprocal (1 ulp; the result
+// is rounded to bf16).
+__device__ __forceinline__ float act_apply_fast(Act a, float u) {
+  if (a == Act::QuickGelu) return u * __builtin_amdgcn_rcpf(1.0f + __expf(-1.702f * u));
+  return act_apply(a, u);
 }
 
 struct EpiStoreF32 {
   static constexpr bool kStaged = true;
   static constexpr int kPatchFloats = 32 * 40;
+  using RowParam = NoRowParam;
+  static constexpr int kRowParamFloats = 0;
   float* C; int ldc; const float* bias;
-  __device__ float pre(int col, float v) const { return v + (bias ? bias[col] : 0.f); }
-  __device__ void store(int row, int col, const float (&v)[4]) const {
+  __device__ float col_param(int col) const { return bias ? bias[col] : 0.f; }
+  __device__ float pre(float cp, float v) const { return v + cp; }
+  __device__ RowParam row_param(int, int) const { return {}; }
+  __device__ void store(int row, int col, const float (&v)[4], const RowParam&) const {
     *reinterpret_cast<float4*>(C + (size_t)row * ldc + col) = make_float4(v[0], v[1], v[2], v[3]);
   }
   template <int FM, int FN>
@@ -89,12 +146,13 @@ struct EpiStoreF32 {
     for (int fn = 0; fn < FN; ++fn) {
       const int col = QV_ACC_COL(wn0, fn, lane);
       if (col >= N) continue;
+      const float cp = col_param(col);
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = QV_ACC_ROW(wm0, fm, r, lane);
-          if (row < M) C[(size_t)row * ldc + col] = pre(col, acc[fm][fn][r]);
+          if (row < M) C[(size_t)row * ldc + col] = pre(cp, acc[fm][fn][r]);
         }
     }
   }
@@ -103,13 +161,17 @@ struct EpiStoreF32 {
 struct EpiResidF32 {
   static constexpr bool kStaged = true;
   static constexpr int kPatchFloats = 32 * 40;
+  using RowParam = float4;
+  static constexpr int kRowParamFloats = 4;
   float* Z; int ldz; const float* bias;
-  __device__ float pre(int col, float v) const { return v + bias[col]; }
-  __device__ void store(int row, int col, const float (&v)[4]) const {
-    float4* p = reinterpret_cast<float4*>(Z + (size_t)row * ldz + col);
-    float4 z = *p;
-    z.x += v[0]; z.y += v[1]; z.z += v[2]; z.w += v[3];
-    *p = z;
+  __device__ float col_param(int col) const { return bias[col]; }
+  __device__ float pre(float cp, float v) const { return v + cp; }
+  __device__ RowParam row_param(int row, int col) const {
+    return *reinterpret_cast<const float4*>(Z + (size_t)row * ldz + col);
+  }
+  __device__ void store(int row, int col, const float (&v)[4], const RowParam& z) const {
+    *reinterpret_cast<float4*>(Z + (size_t)row * ldz + col) =
+        make_float4(z.x + v[0], z.y + v[1], z.z + v[2], z.w + v[3]);
   }
   template <int FM, int FN>
   __device__ void apply_staged(f32x16 (&acc)[FM][FN], float* wlds, int wm0, int wn0, int lane, int M, int N) const {
@@ -121,6 +183,7 @@ struct EpiResidF32 {
     for (int fn = 0; fn < FN; ++fn) {
       const int col = QV_ACC_COL(wn0, fn, lane);
       if (col >= N) continue;
+      const float cp = col_param(col);
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -128,7 +191,7 @@ struct EpiResidF32 {
           const int row = QV_ACC_ROW(wm0, fm, r, lane);
           if (row < M) {
             float* p = Z + (size_t)row * ldz + col;
-            *p = *p + pre(col, acc[fm][fn][r]);
+            *p = *p + pre(cp, acc[fm][fn][r]);
           }
         }
     }
@@ -138,14 +201,18 @@ struct EpiResidF32 {
 struct EpiActBf16 {
   static constexpr bool kStaged = true;
   static constexpr int kPatchFloats = 32 * 40;
+  using RowParam = NoRowParam;
+  static constexpr int kRowParamFloats = 0;
   uint16_t* C; int ldc; const float* bias; Act act;
-  __device__ float pre(int col, float v) const { return act_apply(act, v + bias[col]); }
-  __device__ void store(int row, int col, const float (&v)[8]) const {
+  __device__ float col_param(int col) const { return bias[col]; }
+  __device__ float pre(float cp, float v) const { return act_apply_fast(act, v + cp); }
+  __device__ RowParam row_param(int, int) const { return {}; }
+  __device__ void store(int row, int col, const float (&v)[8], const RowParam&) const {
     uint4 pk;
-    pk.x = bf16_bits(v[0]) | ((uint32_t)bf16_bits(v[1]) << 16);
-    pk.y = bf16_bits(v[2]) | ((uint32_t)bf16_bits(v[3]) << 16);
-    pk.z = bf16_bits(v[4]) | ((uint32_t)bf16_bits(v[5]) << 16);
-    pk.w = bf16_bits(v[6]) | ((uint32_t)bf16_bits(v[7]) << 16);
+    pk.x = pack_bf16(v[0], v[1]);
+    pk.y = pack_bf16(v[2], v[3]);
+    pk.z = pack_bf16(v[4], v[5]);
+    pk.w = pack_bf16(v[6], v[7]);
     *reinterpret_cast<uint4*>(C + (size_t)row * ldc + col) = pk;
   }
   template <int FM, int FN>
@@ -158,12 +225,13 @@ struct EpiActBf16 {
     for (int fn = 0; fn < FN; ++fn) {
       const int col = QV_ACC_COL(wn0, fn, lane);
       if (col >= N) continue;
+      const float cp = col_param(col);
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = QV_ACC_ROW(wm0, fm, r, lane);
-          if (row < M) C[(size_t)row * ldc + col] = bf16_bits(pre(col, acc[fm][fn][r]));
+          if (row < M) C[(size_t)row * ldc + col] = bf16_bits(pre(cp, acc[fm][fn][r]));
         }
     }
   }
@@ -207,57 +275,78 @@ struct EpiQkv {
   // transposed [feature][row] and leaves as 8-byte runs of 4 consecutive keys
   // (a 4-aligned run of packed rows stays inside one image and maps to 4
   // contiguous key slots even after the bits-2/3 key permutation).
+  // As in staged_store, every global load (bias, token info, rotary table)
+  // of a 32-row block is issued before that block's first store.
   template <int FM, int FN>
   __device__ void apply_staged(f32x16 (&acc)[FM][FN], float* wlds, int wm0, int wn0, int lane, int M, int N) const {
     const int dim = o.dim;
     const int c = lane & 31;
     if (wn0 < 2 * dim) {
+      constexpr int NP = FN / 2;  // 64-column groups of rotation pairs
+      float b0[NP], b1[NP];
+      int fi[NP], jj[NP], gg[NP];
 #pragma unroll
-      for (int fp = 0; fp < FN; fp += 2) {
-        const int v0 = wn0 + fp * 32;  // first virtual column of this 64-group
+      for (int fp = 0; fp < NP; ++fp) {
+        const int v0 = wn0 + fp * 64;  // first virtual column of this 64-group
         const int region = v0 >= dim ? 1 : 0;
         const int g = (v0 - region * dim) >> 6;
         const int pair = 32 * g + c;
         const int head = pair / (kHeadDim / 2), j = pair % (kHeadDim / 2);
         const int f0 = region * dim + head * kHeadDim + j;
-        const float b0 = bias[f0], b1 = bias[f0 + kHeadDim / 2];
-        const int fi = j < kRopeFreqs ? j : j - kRopeFreqs;
-        uint16_t* base = reinterpret_cast<uint16_t*>(region ? o.k : o.q);
+        b0[fp] = bias[f0];
+        b1[fp] = bias[f0 + kHeadDim / 2];
+        fi[fp] = j < kRopeFreqs ? j : j - kRopeFreqs;
+        jj[fp] = j;
+        gg[fp] = g;
+      }
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-          const int rb = wm0 + fm * 32;
+      for (int fm = 0; fm < FM; ++fm) {
+        const int rb = wm0 + fm * 32;
+        int pos[16], prow[4];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = rb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          pos[r] = row < M ? o.tokinfo[row].x : 0;
+        }
+#pragma unroll
+        for (int pass = 0; pass < 4; ++pass) {
+          const int row = rb + ((pass * 64 + lane) >> 3);
+          prow[pass] = row < M ? o.tokinfo[row].y : 0;
+        }
+        float2 cs[NP][16];
+#pragma unroll
+        for (int fp = 0; fp < NP; ++fp)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int p = jj[fp] < kRopeFreqs ? (pos[r] & 0xFFFF) : (pos[r] >> 16);
+            cs[fp][r] = o.rope[p * kRopeFreqs + fi[fp]];
+          }
+#pragma unroll
+        for (int fp = 0; fp < NP; ++fp) {
+          uint16_t* base = reinterpret_cast<uint16_t*>(wn0 + fp * 64 >= dim ? o.k : o.q);
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int rl = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            const int row = rb + rl;
-            float y0 = 0.f, y1 = 0.f;
-            if (row < M) {
-              const int2 ti = o.tokinfo[row];
-              const int p = j < kRopeFreqs ? (ti.x & 0xFFFF) : (ti.x >> 16);
-              const float2 cs = o.rope[p * kRopeFreqs + fi];
-              const float x0 = acc[fm][fp][r] + b0, x1 = acc[fm][fp + 1][r] + b1;
-              y0 = x0 * cs.x - x1 * cs.y;
-              y1 = x1 * cs.x + x0 * cs.y;
-            }
-            wlds[rl * 72 + c] = y0;
-            wlds[rl * 72 + 32 + c] = y1;
+            const float x0 = acc[fm][2 * fp][r] + b0[fp], x1 = acc[fm][2 * fp + 1][r] + b1[fp];
+            const bool ok = rb + rl < M;
+            wlds[rl * 72 + c] = ok ? x0 * cs[fp][r].x - x1 * cs[fp][r].y : 0.f;
+            wlds[rl * 72 + 32 + c] = ok ? x1 * cs[fp][r].x + x0 * cs[fp][r].y : 0.f;
           }
 #pragma unroll
           for (int pass = 0; pass < 4; ++pass) {
             const int task = pass * 64 + lane;
             const int rl = task >> 3, h = (task >> 2) & 1, q = task & 3;
-            const int row = rb + rl;
             const float4 a0 = *reinterpret_cast<const float4*>(&wlds[rl * 72 + 32 * h + 8 * q]);
             const float4 a1 = *reinterpret_cast<const float4*>(&wlds[rl * 72 + 32 * h + 8 * q + 4]);
-            if (row < M) {
-              const int p0 = 32 * g + 8 * q;
+            if (rb + rl < M) {
+              const int p0 = 32 * gg[fp] + 8 * q;
               const int hd = p0 / (kHeadDim / 2), j0 = p0 % (kHeadDim / 2);
               uint4 pk;
-              pk.x = bf16_bits(a0.x) | ((uint32_t)bf16_bits(a0.y) << 16);
-              pk.y = bf16_bits(a0.z) | ((uint32_t)bf16_bits(a0.w) << 16);
-              pk.z = bf16_bits(a1.x) | ((uint32_t)bf16_bits(a1.y) << 16);
-              pk.w = bf16_bits(a1.z) | ((uint32_t)bf16_bits(a1.w) << 16);
-              const size_t off = ((size_t)hd * o.P + o.tokinfo[row].y) * kHeadDim + j0 + h * (kHeadDim / 2);
+              pk.x = pack_bf16(a0.x, a0.y);
+              pk.y = pack_bf16(a0.z, a0.w);
+              pk.z = pack_bf16(a1.x, a1.y);
+              pk.w = pack_bf16(a1.z, a1.w);
+              const size_t off = ((size_t)hd * o.P + prow[pass]) * kHeadDim + j0 + h * (kHeadDim / 2);
               *reinterpret_cast<uint4*>(base + off) = pk;
             }
           }
@@ -265,32 +354,38 @@ struct EpiQkv {
       }
     } else {
       uint16_t* vt = reinterpret_cast<uint16_t*>(o.vt);
+      float bb[FN];
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) bb[fn] = bias[wn0 + fn * 32 + c];
+      int pr[FM];  // padded row of this lane's 4-key run, the same in every pass
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        const int row = wm0 + fm * 32 + 4 * (lane & 7);
+        pr[fm] = row < M ? o.tokinfo[row].y : 0;
+      }
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
         const int col0 = wn0 + fn * 32;
-        const float bb = bias[col0 + c];
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
           const int rb = wm0 + fm * 32;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int rl = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            wlds[c * 36 + rl] = acc[fm][fn][r] + bb;
+            wlds[c * 36 + rl] = acc[fm][fn][r] + bb[fn];
           }
+          const int row = rb + 4 * (lane & 7);
+          const int pp = (pr[fm] & ~12) | ((pr[fm] & 4) << 1) | ((pr[fm] & 8) >> 1);
 #pragma unroll
           for (int pass = 0; pass < 4; ++pass) {
-            const int task = pass * 64 + lane;
-            const int cf = task >> 3, g4 = task & 7;
-            const int row = rb + 4 * g4;
-            const float4 a = *reinterpret_cast<const float4*>(&wlds[cf * 36 + 4 * g4]);
+            const int cf = pass * 8 + (lane >> 3);
+            const float4 a = *reinterpret_cast<const float4*>(&wlds[cf * 36 + 4 * (lane & 7)]);
             if (row < M) {
               const int f = col0 + cf - 2 * dim;
               const int hd = f / kHeadDim, dd = f % kHeadDim;
-              const int pr = o.tokinfo[row].y;
-              const int pp = (pr & ~12) | ((pr & 4) << 1) | ((pr & 8) >> 1);
               uint2 pk;
-              pk.x = bf16_bits(a.x) | ((uint32_t)bf16_bits(a.y) << 16);
-              pk.y = bf16_bits(a.z) | ((uint32_t)bf16_bits(a.w) << 16);
+              pk.x = pack_bf16(a.x, a.y);
+              pk.y = pack_bf16(a.z, a.w);
               *reinterpret_cast<uint2*>(vt + ((size_t)hd * kHeadDim + dd) * o.P + pp) = pk;
             }
           }
