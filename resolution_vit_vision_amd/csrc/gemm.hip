@@ -553,23 +553,56 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(const uint16_t* __restrict__ 
   epi.apply(acc, m0 + wm * TM, n0 + wn * TN, lane, M, N);
 }
 
+// XCD cut of the tile grid (see tile_coords): the xgn in {1, 2, 4, 8} whose
+// rectangles need the fewest A + B rows per XCD, and the grid size.
+struct XcdCut {
+  int xgn;
+  unsigned grid;
+};
+static XcdCut xcd_cut(int tiles_m, int tiles_n, int BM, int BN) {
+  XcdCut best{1, 0};
+  int64_t best_rows = -1;
+  for (int xgn = 1; xgn <= 8; xgn *= 2) {
+    const int xgm = 8 / xgn;
+    const int64_t rm = (tiles_m + xgm - 1) / xgm, rn = (tiles_n + xgn - 1) / xgn;
+    const int64_t rows = rm * BM + rn * BN;
+    if (best_rows < 0 || rows < best_rows) {
+      best_rows = rows;
+      best = XcdCut{xgn, (unsigned)(8 * rm * rn)};
+    }
+  }
+  return best;
+}
+
 template <int BM, int BN, int WM, int WN, int ST, int KT, int KS = 1, class Epi, class RowMap>
 static hipError_t launch_pipe(const void* A, int lda, const void* B, int ldb, int M, int N, const Epi& epi,
                               RowMap rmap, hipStream_t s) {
-  const unsigned tiles = (unsigned)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
-  const int raster = M <= 2048 ? 0 : 1;
-  hipLaunchKernelGGL((k_gemm_pipe<BM, BN, WM, WN, ST, KT / KS, KS, Epi, RowMap>), dim3(tiles), dim3(WM * WN * KS * 64), 0, s,
-                     reinterpret_cast<const uint16_t*>(A), lda, reinterpret_cast<const uint16_t*>(B), ldb, M, N,
-                     raster, 8, epi, rmap);
+  const XcdCut cut = xcd_cut((M + BM - 1) / BM, (N + BN - 1) / BN, BM, BN);
+  hipLaunchKernelGGL((k_gemm_pipe<BM, BN, WM, WN, ST, KT / KS, KS, Epi, RowMap>), dim3(cut.grid), dim3(WM * WN * KS * 64),
+                     0, s, reinterpret_cast<const uint16_t*>(A), lda, reinterpret_cast<const uint16_t*>(B), ldb, M, N,
+                     cut.xgn, 8, epi, rmap);
   return hipGetLastError();
 }
 
-// Tile shape by how many output tiles the problem has: 256x256 (8 waves) when
-// that already fills the GPU; 128x160 (4 waves of 32x160) when N is a
+template <int BM, int BN, int WM, int WN, int ST, int KT, int NP, class Epi, class RowMap>
+static hipError_t launch_ws(const void* A, int lda, const void* B, int ldb, int M, int N, const Epi& epi,
+                            RowMap rmap, hipStream_t s) {
+  const XcdCut cut = xcd_cut((M + BM - 1) / BM, (N + BN - 1) / BN, BM, BN);
+  hipLaunchKernelGGL((k_gemm_ws<BM, BN, WM, WN, ST, KT, NP, Epi, RowMap>), dim3(cut.grid), dim3((WM * WN + NP) * 64), 0,
+                     s, reinterpret_cast<const uint16_t*>(A), lda, reinterpret_cast<const uint16_t*>(B), ldb, M, N,
+                     cut.xgn, 8, epi, rmap);
+  return hipGetLastError();
+}
+
+// Tile shape by how many output tiles the problem has: 256x256 (8 waves,
+// direct pipeline) when that already fills the GPU; 128x160 when N is a
 // multiple of 160 and that tiling fills one wave of 256 workgroups (the
-// 448x448 image's MLP up-projection: 8 x 32 tiles); 128x128 (8 waves) for
-// other mid sizes; 64x128 when N is narrow and M small.  The q/k/v epilogue
-// needs wave tiles whose width is a multiple of 64, which 32x160 is not.
+// 448x448 image's MLP up-projection: 8 x 32 tiles); 128x128 for other mid
+// sizes; 64x128 with the K split over two wave groups when N is narrow and M
+// small.  The 128x160 and 128x128 tilings run warp-specialized (producer
+// waves own the LDS-DMA), which measured 5-15% faster there.  The q/k/v
+// epilogue needs wave tiles whose width is a multiple of 64, which 32x160
+// is not.
 template <int KT, bool ALLOW160, class Epi, class RowMap>
 static hipError_t run_pipe(const void* A, int lda, const void* B, int ldb, int M, int N, const Epi& epi,
                            RowMap rmap, hipStream_t s) {
@@ -579,8 +612,8 @@ static hipError_t run_pipe(const void* A, int lda, const void* B, int ldb, int M
   if (t256 >= 256) return launch_pipe<256, 256, 2, 4, 2, KT>(A, lda, B, ldb, M, N, epi, rmap, s);
   if constexpr (ALLOW160)
     if (N % 160 == 0 && t160 >= 192 && t160 <= 256)
-      return launch_pipe<128, 160, 4, 1, 4, KT>(A, lda, B, ldb, M, N, epi, rmap, s);
-  if (t128 >= 200) return launch_pipe<128, 128, 4, 2, 4, KT>(A, lda, B, ldb, M, N, epi, rmap, s);
+      return launch_ws<128, 160, 4, 1, 4, KT, 4>(A, lda, B, ldb, M, N, epi, rmap, s);
+  if (t128 >= 200) return launch_ws<128, 128, 4, 2, 4, KT, 2>(A, lda, B, ldb, M, N, epi, rmap, s);
   // few tiles: two wave groups split K inside each workgroup
   return launch_pipe<64, 128, 2, 2, 3, KT, 2>(A, lda, B, ldb, M, N, epi, rmap, s);
 }

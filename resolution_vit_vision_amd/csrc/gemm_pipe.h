@@ -148,39 +148,31 @@ __device__ __forceinline__ void pipe_compute(const uint16_t* stage, f32x16 (&acc
 }
 
 // Tile order.  Workgroups are dispatched round-robin over the 8 XCDs
-// (workgroup b runs on XCD b % 8), and each XCD has its own L2.  `raster`
-// selects how the tile grid is cut between XCDs:
-//   raster 0: XCD x owns a contiguous band of column tiles (all row tiles),
-//             so each weight panel is fetched into exactly one L2 and the
-//             (small) activation matrix is replicated: right when M is small;
-//   raster 1: XCD x owns a contiguous band of row tiles, and inside the band
-//             tiles are visited in groups of `group` row tiles sweeping the
-//             column tiles, so the weight panels in flight are shared by
-//             `group` concurrent row tiles: right when M is large.
-__device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int raster, int group, int& tm,
+// (workgroup b runs on XCD b % 8), and each XCD fills its own L2 from the
+// Infinity Cache / HBM.  The tile grid is cut into an xgm x xgn grid of
+// rectangles (xgm * xgn = 8), one per XCD, so an XCD fetches only the A rows
+// and B rows of its rectangle; the host picks the cut that minimizes those
+// bytes (tm_rows * BM + tn_cols * BN per XCD).  Inside a rectangle tiles go in
+// groups of `group` row tiles sweeping the column tiles, so the panels in
+// flight are shared by concurrent workgroups.  Rectangles differ by at most
+// one row / column tile; the grid has 8 x (largest rectangle) workgroups and
+// the surplus ones of smaller rectangles return at once (valid = false).
+__device__ __forceinline__ bool tile_coords(int bid, int tiles_m, int tiles_n, int xgn, int group, int& tm,
                                             int& tn) {
-  const int total = tiles_m * tiles_n;
-  if (raster == 0) {
-    if (tiles_n % 8 == 0) {
-      const int per_x = tiles_n / 8;            // column tiles per XCD
-      const int x = bid % 8, i = bid / 8;       // i-th workgroup of XCD x
-      tm = i % tiles_m;
-      tn = x * per_x + i / tiles_m;
-    } else {
-      tm = bid % tiles_m;
-      tn = bid / tiles_m;
-    }
-    return;
-  }
-  int t = bid;
-  if (total % 8 == 0) t = (bid % 8) * (total / 8) + bid / 8;
-  // grouped order over the linear index t
-  const int per_group = group * tiles_n;
-  const int g = t / per_group, first_m = g * group;
-  const int gm = (tiles_m - first_m) < group ? (tiles_m - first_m) : group;
-  const int r = t % per_group;
-  tm = first_m + r % gm;
-  tn = r / gm;
+  const int xgm = 8 / xgn;
+  const int x = bid % 8, i = bid / 8;
+  const int gx = x / xgn, gy = x % xgn;
+  const int tm0 = gx * tiles_m / xgm, tm1 = (gx + 1) * tiles_m / xgm;
+  const int tn0 = gy * tiles_n / xgn, tn1 = (gy + 1) * tiles_n / xgn;
+  const int rm = tm1 - tm0, rn = tn1 - tn0;
+  if (i >= rm * rn) return false;
+  const int per_group = group * rn;
+  const int g = i / per_group, first = g * group;
+  const int gsz = (rm - first) < group ? (rm - first) : group;
+  const int r = i % per_group;
+  tm = tm0 + first + r % gsz;
+  tn = tn0 + r / gsz;
+  return true;
 }
 
 // Statically unrolled K loop: with no loop-carried merge point the compiler
@@ -207,7 +199,7 @@ struct PipeSteps {
 template <int BM, int BN, int WM, int WN, int STAGES, int KT, int KS, class Epi, class RowMap>
 __global__ __launch_bounds__(WM * WN * KS * 64) void k_gemm_pipe(const uint16_t* __restrict__ A, int lda,
                                                                  const uint16_t* __restrict__ B, int ldb, int M,
-                                                                 int N, int raster, int group, Epi epi, RowMap rmap) {
+                                                                 int N, int xgn, int group, Epi epi, RowMap rmap) {
   using C = PipeCfg<BM, BN, WM, WN, STAGES, KS>;
   constexpr int SE = C::STAGE_ELEMS;
   __shared__ __attribute__((aligned(1024))) uint16_t st0[SE];
@@ -226,7 +218,7 @@ __global__ __launch_bounds__(WM * WN * KS * 64) void k_gemm_pipe(const uint16_t*
   const int wm = wig / WN, wn = wig % WN;
   const int tiles_n = (N + BN - 1) / BN, tiles_m = (M + BM - 1) / BM;
   int tm, tn;
-  tile_coords(blockIdx.x, tiles_m, tiles_n, raster, group, tm, tn);
+  if (!tile_coords(blockIdx.x, tiles_m, tiles_n, xgn, group, tm, tn)) return;  // uniform over the workgroup
   const int m0 = tm * BM, n0 = tn * BN;
 
   PipeState<C> ps;
@@ -281,6 +273,141 @@ __global__ __launch_bounds__(WM * WN * KS * 64) void k_gemm_pipe(const uint16_t*
   } else {
     epi.apply(acc, m0 + wm * C::TM, n0 + wn * C::TN, lane, M, N);
   }
+}
+
+// ------------------------------------------------------- warp-specialized
+// The address unit of a CU moves 64 bytes per clock, so one 1 KB LDS-DMA
+// instruction occupies it for 16 clocks; a wave that issues its share of a
+// stage while the unit is saturated stalls at issue, and its matrix pipe
+// idles.  Here NP producer waves issue every load of the ring and never
+// touch the MFMA pipe, while WM x WN consumer waves only read LDS and
+// multiply.  Both roles meet at one workgroup barrier per k-step: barrier kt
+// publishes stage kt (its producer-side vmcnt wait came first) and tells
+// the producers that stage kt - 1 (its buffer is refilled next) is free.
+// Producers also take part in the barrier that ends the main loop, so both
+// roles execute the same number of barriers.
+template <int BM, int BN, int NP, int LP, class RowMap>
+__device__ __forceinline__ void ws_setup(const char* (&gsrc)[LP], uint32_t (&ldst)[LP], const uint16_t* A, int lda,
+                                         const uint16_t* B, int ldb, int M, int N, int m0, int n0, int pw,
+                                         int lane, RowMap rmap) {
+#pragma unroll
+  for (int i = 0; i < LP; ++i) {
+    const int blk = i * NP + pw;                // 1 KB block of the stage
+    const int q = blk * 64 + lane;              // 16-byte slot
+    const bool isA = q < BM * 8;
+    const int qq = isA ? q : q - BM * 8;
+    const int r = qq >> 3;
+    const int c = swz_chunk(r, qq & 7);
+    if (isA) {
+      int g = m0 + r;
+      g = g < M ? g : M - 1;
+      gsrc[i] = reinterpret_cast<const char*>(A + (size_t)g * lda + c * 8);
+    } else {
+      int g = n0 + r;
+      g = g < N ? g : N - 1;
+      gsrc[i] = reinterpret_cast<const char*>(B + (size_t)rmap(g) * ldb + c * 8);
+    }
+    ldst[i] = (uint32_t)(blk * 1024);
+  }
+}
+
+template <int LP>
+__device__ __forceinline__ void ws_issue(const char* const (&gsrc)[LP], const uint32_t (&ldst)[LP], uint16_t* stage,
+                                         int kt) {
+#pragma unroll
+  for (int i = 0; i < LP; ++i)
+    __builtin_amdgcn_global_load_lds((gas_ptr)(gsrc[i] + (size_t)kt * 128),
+                                     (las_ptr)(reinterpret_cast<char*>(stage) + ldst[i]), 16, 0, 0);
+}
+
+template <int KT, int STAGES, int LP>
+struct WsProducer {
+  template <int kt>
+  static __device__ __forceinline__ void run(uint16_t* const (&st)[8], const char* const (&gsrc)[LP],
+                                             const uint32_t (&ldst)[LP]) {
+    if constexpr (kt < KT) {
+      constexpr int later = (KT - 1 - kt) < (STAGES - 2) ? (KT - 1 - kt) : (STAGES - 2);
+      QV_WAIT_VM(later * LP);
+      QV_BARRIER();
+      if constexpr (kt + STAGES - 1 < KT) ws_issue<LP>(gsrc, ldst, st[(kt + STAGES - 1) % STAGES], kt + STAGES - 1);
+      run<kt + 1>(st, gsrc, ldst);
+    }
+  }
+};
+
+template <class C, int KT, int STAGES>
+struct WsConsumer {
+  template <int kt>
+  static __device__ __forceinline__ void run(uint16_t* const (&st)[8], f32x16 (&acc)[C::FM][C::FN], int wm, int wn,
+                                             int lane) {
+    if constexpr (kt < KT) {
+      QV_BARRIER();
+      pipe_compute<C>(st[kt % STAGES], acc, wm, wn, lane);
+      run<kt + 1>(st, acc, wm, wn, lane);
+    }
+  }
+};
+
+template <int BM, int BN, int WM, int WN, int STAGES, int KT, int NP, class Epi, class RowMap>
+__global__ __launch_bounds__((WM * WN + NP) * 64) void k_gemm_ws(const uint16_t* __restrict__ A, int lda,
+                                                                const uint16_t* __restrict__ B, int ldb, int M,
+                                                                int N, int xgn, int group, Epi epi, RowMap rmap) {
+  using C = PipeCfg<BM, BN, WM, WN, STAGES, 1>;
+  constexpr int NC = WM * WN;
+  constexpr int BLOCKS = (BM + BN) * 8 / 64;  // 1 KB blocks per stage
+  constexpr int LP = BLOCKS / NP;
+  static_assert(BLOCKS % NP == 0, "stage blocks split evenly over the producers");
+  static_assert(LP * (STAGES - 1) <= 63, "producer loads in flight fit the 6-bit vmcnt");
+  constexpr int SE = C::STAGE_ELEMS;
+  __shared__ __attribute__((aligned(1024))) uint16_t st0[SE];
+  __shared__ __attribute__((aligned(1024))) uint16_t st1[SE];
+  __shared__ __attribute__((aligned(1024))) uint16_t st2[STAGES > 2 ? SE : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t st3[STAGES > 3 ? SE : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t st4[STAGES > 4 ? SE : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t st5[STAGES > 5 ? SE : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t st6[STAGES > 6 ? SE : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t st7[STAGES > 7 ? SE : 8];
+  uint16_t* const st[8] = {st0, st1, st2, st3, st4, st5, st6, st7};
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tiles_n = (N + BN - 1) / BN, tiles_m = (M + BM - 1) / BM;
+  int tm, tn;
+  if (!tile_coords(blockIdx.x, tiles_m, tiles_n, xgn, group, tm, tn)) return;  // uniform over the workgroup
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  if (wave >= NC) {
+    const char* gsrc[LP];
+    uint32_t ldst[LP];
+    ws_setup<BM, BN, NP, LP>(gsrc, ldst, A, lda, B, ldb, M, N, m0, n0, wave - NC, lane, rmap);
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+      if (s < KT) ws_issue<LP>(gsrc, ldst, st[s], s);
+    WsProducer<KT, STAGES, LP>::template run<0>(st, gsrc, ldst);
+    QV_BARRIER();  // pairs with the consumers' end-of-loop barrier
+    return;
+  }
+
+  const int wm = wave / WN, wn = wave % WN;
+  f32x16 acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  WsConsumer<C, KT, STAGES>::template run<0>(st, acc, wm, wn, lane);
+
+  // every consumer is done reading the ring and every load has landed
+  constexpr int SLOT = Epi::kPatchFloats;
+  constexpr int PER = (SE * 2) / (SLOT * 4);
+  static_assert(PER >= 1 && PER * STAGES >= NC, "per-wave slots fit in the ring");
+  QV_BARRIER();
+  const int sb = wave / PER;
+  uint16_t* sbuf = sb == 0 ? st0 : sb == 1 ? st1 : sb == 2 ? st2 : sb == 3 ? st3 : sb == 4 ? st4 : sb == 5 ? st5
+                 : sb == 6 ? st6 : st7;
+  float* slot = reinterpret_cast<float*>(sbuf) + (wave % PER) * SLOT;
+  epi.apply_staged(acc, slot, m0 + wm * C::TM, n0 + wn * C::TN, lane, M, N);
 }
 
 }  // namespace qv

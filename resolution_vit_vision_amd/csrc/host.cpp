@@ -72,6 +72,41 @@ std::pair<hipEvent_t, hipEvent_t>* timing_slot(int cls) {
     if (slot_) QV_HIP(hipEventRecord(slot_->second, stream));              \
   } while (0)
 
+// Weight warm-up: a side stream (default priority) on which small read-only
+// kernels pull the next GEMMs' weights into the Infinity Cache while the
+// current kernels run.  Created once per device and kept for the life of the
+// process; `mu` serializes the enqueue of forwards that share it, because
+// the events are reused from call to call.
+struct WarmCtx {
+  std::mutex mu;
+  hipStream_t side = nullptr;
+  std::vector<hipEvent_t> ev;  // one per block
+  hipEvent_t done = nullptr;
+};
+
+WarmCtx* warm_ctx(int depth) {
+  static std::mutex mu;
+  static WarmCtx per_dev[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> g(mu);
+  WarmCtx& w = per_dev[dev];
+  if (!w.side && hipStreamCreateWithFlags(&w.side, hipStreamNonBlocking) != hipSuccess) {
+    w.side = nullptr;
+    return nullptr;
+  }
+  if (!w.done && hipEventCreateWithFlags(&w.done, hipEventDisableTiming) != hipSuccess) {
+    w.done = nullptr;
+    return nullptr;
+  }
+  while ((int)w.ev.size() < depth) {
+    hipEvent_t e;
+    if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return nullptr;
+    w.ev.push_back(e);
+  }
+  return &w;
+}
+
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -399,8 +434,23 @@ qv_status qv_vision_forward(const qv_vision_cfg* c, const qv_vision_w* w, const 
                           c->patch_dim, M, D, c->patch_dim, reinterpret_cast<const float*>(w->patch_b), hidden, D, s));
 
   AttnArgs aa{qo.q, qo.k, qo.vt, O, D, cu_seqlens, plan, n_img, (int)vp.P, c->heads, vp.total_qtiles, vp.attn_rows};
+  // bf16 path: at the start of block l the side stream warms block l's
+  // proj / fc1 / fc2 weights and block l + 1's qkv weights, in the order the
+  // GEMMs need them; the caller's stream waits for the side stream at the end.
+  WarmCtx* wc = (bf && c->depth > 0) ? warm_ctx(c->depth) : nullptr;
+  std::unique_lock<std::mutex> warm_lock;
+  if (wc) warm_lock = std::unique_lock<std::mutex>(wc->mu);
+  const size_t wb = 2;  // bf16 weights
   for (int l = 0; l < c->depth; ++l) {
     const qv_block_w& b = w->blocks[l];
+    if (wc) {
+      QV_HIP(hipEventRecord(wc->ev[l], s));
+      QV_HIP(hipStreamWaitEvent(wc->side, wc->ev[l], 0));
+      QV_HIP(launch_warm(b.proj_w, (size_t)D * D * wb, wc->side));
+      QV_HIP(launch_warm(b.fc1_w, (size_t)F * D * wb, wc->side));
+      QV_HIP(launch_warm(b.fc2_w, (size_t)D * F * wb, wc->side));
+      if (l + 1 < c->depth) QV_HIP(launch_warm(w->blocks[l + 1].qkv_w, (size_t)3 * D * D * wb, wc->side));
+    }
     QV_LAUNCH(QV_KC_LAYERNORM, s, launch_layernorm(hidden, (const float*)b.ln1_w, (const float*)b.ln1_b, A, bf, M, D, c->ln_eps, s));
     if (bf) {
       QV_LAUNCH(QV_KC_QKV, s, gemm_bf16_qkv(A, D, b.qkv_w, D, M, D, (const float*)b.qkv_b, qo, s));
@@ -425,6 +475,10 @@ qv_status qv_vision_forward(const qv_vision_cfg* c, const qv_vision_w* w, const 
       QV_LAUNCH(QV_KC_FC2, s, gemm_f32_resid((const float*)H, F, (const float*)b.fc2_w, F, M, D, F, (const float*)b.fc2_b, hidden, D,
                             s));
     }
+  }
+  if (wc) {
+    QV_HIP(hipEventRecord(wc->done, wc->side));
+    QV_HIP(hipStreamWaitEvent(s, wc->done, 0));
   }
   return QV_OK;
 }

@@ -150,6 +150,36 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------ cache warm-up
+// Reads `bytes` of `src` (16-byte multiple) so that they pass through L2 and
+// stay in the Infinity Cache for a kernel that runs a little later on another
+// stream: the GEMMs stream their weights once per forward, and a cold weight
+// panel costs them HBM latency they cannot hide in LDS.  One wave per
+// workgroup, LDS-DMA into a 1 KB sink (nothing is kept or waited on per
+// load), at most 24 loads in flight per wave; the wave drains its loads
+// before it ends so no DMA write can land in LDS the workgroup no longer owns.
+#define QV_WARM_WAIT_VM(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 0xF) | 0x70 | 0xF00 | ((((n) >> 4) & 3) << 14))
+__global__ __launch_bounds__(64) void k_warm(const char* __restrict__ src, size_t bytes) {
+  __shared__ __attribute__((aligned(1024))) char sink[1024];
+  typedef const __attribute__((address_space(1))) void* gas_ptr;
+  typedef __attribute__((address_space(3))) void* las_ptr;
+  const int lane = threadIdx.x;
+  int n = 0;
+  for (size_t off = (size_t)blockIdx.x * 1024; off < bytes; off += (size_t)gridDim.x * 1024) {
+    const size_t at = off + (size_t)lane * 16;
+    if (at < bytes) __builtin_amdgcn_global_load_lds((gas_ptr)(src + at), (las_ptr)sink, 16, 0, 0);
+    if (++n >= 24) QV_WARM_WAIT_VM(23);
+  }
+  QV_WARM_WAIT_VM(0);
+}
+
+hipError_t launch_warm(const void* src, size_t bytes, hipStream_t s) {
+  if (!src || bytes < 16) return hipSuccess;
+  hipLaunchKernelGGL(k_warm, dim3(64), dim3(64), 0, s, reinterpret_cast<const char*>(src), bytes & ~(size_t)15);
+  return hipGetLastError();
+}
+
 // ----------------------------------------------------------------- LayerNorm
 // One wave64 per row of NV*256 floats: each lane holds NV float4.  Statistics
 // in float32: mean, then the mean of squared deviations (two passes over
