@@ -4,13 +4,15 @@
 // in the sequence and nothing of size n^2 is stored.
 //
 // Layouts (written by the q/k/v projection epilogue):
-//   Q, K  [heads][P][80]   bf16/f32, image i's rows start at prow0_i
+//   Q     [heads][P][80]                    bf16 / f32
+//   K     bf16: key-tiled [heads][P/32][10][32][8] (kc_offset); f32: [heads][P][80]
 //   V^T   [heads][80][P]   (transposed so P.V reads keys contiguously)
-// prow0_i is a multiple of 128 and rows past an image's end are zero.
-// Output O is packed [N][ldo] with head h in columns 80h .. 80h+79.
+// image i's rows start at prow0_i, a multiple of 128, and rows past an
+// image's end are zero.  Output O is packed [N][ldo] with head h in columns
+// 80h .. 80h+79.
 //
 // bf16 kernel (gfx950 MFMA, wave64): each wave owns 32 query rows of one
-// (image, head) and a share of the keys.  Per 32-key block a wave forms
+// (image, head) and a share of the keys.  Per 32-key tile a wave forms
 // S^T = K . Q^T with v_mfma_f32_32x32x16_bf16 (5 k-steps over the 80 head
 // elements, so no padding), which leaves each lane holding one query column.
 // That register layout is directly the B operand of O^T = V^T . P^T, so P
@@ -18,12 +20,10 @@
 // 32-row MFMA blocks); row 80 of V^T is a row of ones, so O^T row 80
 // accumulates the softmax denominator for free, with the same bf16-rounded P
 // as the numerator.
+#include "gemm_pipe.h"  // MFMA operand types, LDS-DMA pointer types, wait / barrier macros
 #include "qv_internal.h"
 
 namespace qv {
-
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -49,39 +49,49 @@ __device__ __forceinline__ int find_plan(const PlanEntry* plan, int n_img, int g
   return lo;
 }
 
-// Work split.  A workgroup is 4 waves = QW query groups x KW key groups.
-// Wave (qw, kw) owns query rows 32 qw .. 32 qw + 31 of the workgroup's tile
-// and, in every iteration, the kw-th sub-tile of KT keys of the KW * KT keys
-// staged in LDS.  With KW > 1 the partial (max, numerator, denominator) of
-// the KW key groups are combined through LDS at the end, so short images
-// still give the GPU enough workgroups.
+// Work split.  A workgroup is 8 waves = QW query groups x KW key groups (two
+// waves per SIMD, so one wave's softmax arithmetic overlaps the other's
+// matrix work).  Wave (qw, kw) owns query rows 32 qw .. 32 qw + 31 of the
+// workgroup's BQ = 32 QW rows and, of every stage of IK = 32 KW keys, the
+// kw-th 32-key tile.  The partial (max, numerator, denominator) of the KW key
+// groups are combined through LDS at the end.
 //
+// Keys stream through a ring of 4 LDS stages filled by LDS-DMA (every wave
+// issues its share of each stage's 1 KB blocks three stages ahead).  A stage is
+//   K   : IK / 32 key tiles x 10 chunks x 32 keys x 16 B, a verbatim copy of
+//         the key-tiled global layout (kc_offset), so a wave's operand read
+//         of one chunk is 32 consecutive 16-byte slots;
+//   V^T : 80 dims x IK keys, 16-byte key chunks XOR-swizzled by dim so the
+//         32 dims a half-wave reads land on distinct bank groups.
 // V^T keys are stored permuted inside each group of 16 (bits 2 and 3 of the
 // key index swapped, done by the q/k/v epilogue): the 8 keys one lane of the
 // P.V operand needs are then contiguous, one 16-byte LDS read.
-template <int KT>
+template <int IK>
 __device__ __forceinline__ int v_swz(int d, int chunk) {
-  return KT == 32 ? (chunk ^ ((d >> 2) & 3)) : (chunk ^ ((d >> 1) & 7));
+  return IK == 128 ? (chunk ^ (d & 15)) : (chunk ^ ((d >> 1) & 7));
 }
 
-template <int KW, int KT>
-__global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a, float scale_log2) {
-  constexpr int QW = 4 / KW;
+template <int QW, int KW>
+__global__ __launch_bounds__(512) void k_attn_bf16(AttnArgs a, float scale_log2) {
+  constexpr int NWV = QW * KW;
+  static_assert(NWV == 8, "eight waves");
   constexpr int BQ = 32 * QW;
-  constexpr int IK = KW * KT;             // keys staged per iteration
-  constexpr int NCH = IK * kHeadDim / 8;  // 16-byte chunks of K (and of V^T) per iteration
-  constexpr int PER_T = (NCH + 255) / 256;
-  constexpr int SB = KT / 32;             // 32-key S^T blocks per wave sub-tile
-  // LDS: K rows of 80 elements, then V^T as [kw][80][KT]; reused for the combine
-  constexpr int K_ELEMS = IK * kHeadDim;
-  constexpr int V_ELEMS = KW * kHeadDim * KT;
+  constexpr int IK = 32 * KW;                 // keys per stage
+  static_assert(IK == 64 || IK == 128, "stage of 64 or 128 keys (images are padded to 128)");
+  constexpr int K_SLOTS = IK * (kHeadDim / 8);    // 16-byte slots of K per stage
+  constexpr int V_SLOTS = kHeadDim * (IK / 8);    // of V^T
+  constexpr int STAGE_BYTES = (K_SLOTS + V_SLOTS) * 16;
+  constexpr int BLKS = STAGE_BYTES / 1024;        // LDS-DMA instructions per stage
+  static_assert(STAGE_BYTES % 1024 == 0, "whole KB per stage");
+  constexpr int LW = BLKS / NWV;                  // per wave and stage, at least
+  constexpr int LWMAX = (BLKS + NWV - 1) / NWV;
+  constexpr int NST = 4;
   constexpr int COMB_FLOATS = (KW > 1 ? (KW - 1) * QW * 49 * 64 : 1);
-  constexpr int LDS_BYTES = (2 * (K_ELEMS + V_ELEMS) > 4 * COMB_FLOATS) ? 2 * (K_ELEMS + V_ELEMS) : 4 * COMB_FLOATS;
-  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
-  uint16_t* sK = reinterpret_cast<uint16_t*>(lds);
-  uint16_t* sV = sK + K_ELEMS;
+  constexpr int LDS_BYTES = (NST * STAGE_BYTES > 4 * COMB_FLOATS) ? NST * STAGE_BYTES : 4 * COMB_FLOATS;
+  __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hlf = lane >> 5, l32 = lane & 31;
   const int qw = wave / KW, kw = wave % KW;
   // Flat grid over (head, q-tile).  Workgroup b runs on XCD b % 8; when the
@@ -105,43 +115,42 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a, float scale_log2)
   const int qbase = (gt - pe.qtile0) * BQ + qw * 32;
 
   const uint16_t* Qh = reinterpret_cast<const uint16_t*>(a.q) + (size_t)head * a.P * kHeadDim;
-  const uint16_t* Kh = reinterpret_cast<const uint16_t*>(a.k) + (size_t)head * a.P * kHeadDim;
-  const uint16_t* Vh = reinterpret_cast<const uint16_t*>(a.vt) + (size_t)head * kHeadDim * a.P;
+  const char* Kt = reinterpret_cast<const char*>(a.k) + kc_offset(head, a.P, pe.prow0, 0) * 2;
+  const char* Vh = reinterpret_cast<const char*>(a.vt) + (size_t)head * kHeadDim * a.P * 2;
 
-  bf16x8 qf[5];
-  {
-    const uint16_t* qr = Qh + (size_t)(pe.prow0 + qbase + l32) * kHeadDim + 8 * hlf;
+  // this wave's LDS-DMA blocks of a stage: blocks wave, wave + 8, ...
+  const char* gsrc[LWMAX];
+  uint32_t ldst[LWMAX];
 #pragma unroll
-    for (int kk = 0; kk < 5; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qr + 16 * kk);
+  for (int i = 0; i < LWMAX; ++i) {
+    int blk = wave + NWV * i;
+    blk = blk < BLKS ? blk : BLKS - 1;  // (only used when i < count)
+    const int slot = blk * 64 + lane;
+    if (slot < K_SLOTS) {
+      gsrc[i] = Kt + (size_t)slot * 16;
+    } else {
+      const int sv = slot - K_SLOTS;
+      const int d = sv / (IK / 8), p = sv % (IK / 8);
+      const int c = v_swz<IK>(d, p);
+      gsrc[i] = Vh + ((size_t)d * a.P + pe.prow0 + 8 * c) * 2;
+    }
+    ldst[i] = (uint32_t)(blk * 1024);
+  }
+  const int nblk = (BLKS - wave + NWV - 1) / NWV;  // blocks this wave issues per stage
+#define QV_ATTN_ISSUE(IT)                                                                                      \
+  {                                                                                                            \
+    char* stage_ = lds + ((IT) % NST) * STAGE_BYTES;                                                           \
+    const size_t kstep_ = (size_t)(IT) * IK * 160; /* K: IK keys x 160 B, contiguous */                       \
+    const size_t vstep_ = (size_t)(IT) * IK * 2;   /* V^T: IK keys along each row */                          \
+    _Pragma("unroll") for (int i = 0; i < LWMAX; ++i) {                                                        \
+      if (i < nblk) {                                                                                          \
+        const bool isk_ = (int)ldst[i] < K_SLOTS * 16;                                                         \
+        __builtin_amdgcn_global_load_lds((gas_ptr)(gsrc[i] + (isk_ ? kstep_ : vstep_)),                       \
+                                         (las_ptr)(stage_ + ldst[i]), 16, 0, 0);                               \
+      }                                                                                                        \
+    }                                                                                                          \
   }
 
-  uint4 rk[PER_T], rv[PER_T];
-#pragma unroll
-  for (int i = 0; i < PER_T; ++i) rk[i] = rv[i] = make_uint4(0, 0, 0, 0);
-#define QV_ATTN_GLOAD(IT)                                                                                  \
-  {                                                                                                        \
-    const int key0 = pe.prow0 + (IT) * IK;                                                                 \
-    _Pragma("unroll") for (int i = 0; i < PER_T; ++i) {                                                    \
-      const int c = tid + 256 * i;                                                                         \
-      if (NCH % 256 == 0 || c < NCH) {                                                                     \
-        rk[i] = *reinterpret_cast<const uint4*>(Kh + (size_t)(key0 + c / 10) * kHeadDim + (c % 10) * 8);  \
-        const int d = c / (IK / 8), g = c % (IK / 8);                                                      \
-        rv[i] = *reinterpret_cast<const uint4*>(Vh + (size_t)d * a.P + key0 + g * 8);                      \
-      }                                                                                                    \
-    }                                                                                                      \
-  }
-#define QV_ATTN_SSTORE()                                                                                   \
-  {                                                                                                        \
-    _Pragma("unroll") for (int i = 0; i < PER_T; ++i) {                                                    \
-      const int c = tid + 256 * i;                                                                         \
-      if (NCH % 256 == 0 || c < NCH) {                                                                     \
-        *reinterpret_cast<uint4*>(&sK[(c / 10) * kHeadDim + (c % 10) * 8]) = rk[i];                        \
-        const int d = c / (IK / 8), g = c % (IK / 8);                                                      \
-        const int w = g / (KT / 8), cc = g % (KT / 8);                                                     \
-        *reinterpret_cast<uint4*>(&sV[(w * kHeadDim + d) * KT + (v_swz<KT>(d, cc) << 3)]) = rv[i];         \
-      }                                                                                                    \
-    }                                                                                                      \
-  }
 
   f32x16 o[3];
 #pragma unroll
@@ -158,79 +167,110 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a, float scale_log2)
   }
 
   const int iters = (n + IK - 1) / IK;
-  QV_ATTN_GLOAD(0)
-  for (int it = 0; it < iters; ++it) {
-    __syncthreads();
-    QV_ATTN_SSTORE()
-    __syncthreads();
-    if (it + 1 < iters) QV_ATTN_GLOAD(it + 1)
-    const int kb = it * IK + kw * KT;  // first key of this wave's sub-tile
-    if (kb >= n) continue;             // wave-uniform: sub-tile entirely past the image
 
-    f32x16 s[SB];
+  // Software pipeline over stages: the scores S^T of stage it + 1 are formed
+  // in the same basic block as the softmax and P.V of stage it, so their
+  // MFMAs can overlap the exp work.  Tiles past the image are computed and
+  // fully masked (they add exact zeros), which keeps every wave in one
+  // instruction stream; the running max starts at a large finite negative
+  // so a fully masked first tile yields p = 0, not NaN.
+  // Ring of NST = 4 buffers, loads issued three stages ahead; the buffer of
+  // stage it + 3 is that of stage it - 1, whose P.V every wave finished before
+  // the barrier that publishes stage it + 1.
+#define QV_ATTN_S(IT, SACC)                                                                                    \
+  {                                                                                                            \
+    const uint16_t* sK_ = reinterpret_cast<const uint16_t*>(lds + ((IT) % NST) * STAGE_BYTES) +               \
+                          kw * (kHeadDim / 8) * 32 * 8;                                                        \
+    _Pragma("unroll") for (int r = 0; r < 16; ++r) SACC[r] = 0.f;                                             \
+    _Pragma("unroll") for (int kk = 0; kk < 5; ++kk) SACC = __builtin_amdgcn_mfma_f32_32x32x16_bf16(          \
+        *reinterpret_cast<const bf16x8*>(sK_ + ((2 * kk + hlf) * 32 + l32) * 8), qf[kk], SACC, 0, 0, 0);    \
+  }
+#define QV_ATTN_MASK(IT, SACC)                                                                                 \
+  {                                                                                                            \
+    const int kb_ = (IT) * IK + kw * 32;                                                                       \
+    if (kb_ + 32 > n) {                                                                                        \
+      _Pragma("unroll") for (int r = 0; r < 16; ++r) {                                                        \
+        const int key_ = kb_ + 8 * (r >> 2) + 4 * hlf + (r & 3);                                               \
+        if (key_ >= n) SACC[r] = -INFINITY;                                                                    \
+      }                                                                                                        \
+    }                                                                                                          \
+  }
+
+  QV_ATTN_ISSUE(0)
+  bf16x8 qf[5];
+  {
+    // stage 0 and this wave's q fragments are waited for together, before
+    // stages 1 and 2 are issued, so the q registers are complete at a point
+    // the compiler can see and no vmcnt wait for them lands in the loop
+    // (where it would also drain the ring's loads)
+    const uint16_t* qr = Qh + (size_t)(pe.prow0 + qbase + l32) * kHeadDim + 8 * hlf;
 #pragma unroll
-    for (int sb = 0; sb < SB; ++sb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[sb][r] = 0.f;
-      const uint16_t* kr = &sK[(kw * KT + 32 * sb + l32) * kHeadDim + 8 * hlf];
-#pragma unroll
-      for (int kk = 0; kk < 5; ++kk)
-        s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kr + 16 * kk), qf[kk],
-                                                         s[sb], 0, 0, 0);
+    for (int kk = 0; kk < 5; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qr + 16 * kk);
+  }
+  QV_WAIT_VM(0);
+  QV_BARRIER();
+  if (iters > 1) QV_ATTN_ISSUE(1)
+  if (iters > 2) QV_ATTN_ISSUE(2)
+  m_run = -1.0e30f;
+  f32x16 s_cur, s_nxt;
+  QV_ATTN_S(0, s_cur)
+  for (int it = 0; it < iters; ++it) {
+    if (it + 1 < iters) {
+      if (it + 2 < iters) QV_WAIT_VM(LW);
+      else QV_WAIT_VM(0);
+      QV_BARRIER();
+      if (it + 3 < iters) QV_ATTN_ISSUE(it + 3)
     }
-    if (kb + KT > n) {
+    QV_ATTN_MASK(it, s_cur)
+    float mx = s_cur[0];
 #pragma unroll
-      for (int sb = 0; sb < SB; ++sb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb + 32 * sb + 8 * (r >> 2) + 4 * hlf + (r & 3);
-          if (key >= n) s[sb][r] = -INFINITY;
-        }
-    }
-    float mx = s[0][0];
-#pragma unroll
-    for (int sb = 0; sb < SB; ++sb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s_cur[r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float cand = mx * scale_log2;
-    const bool grow = cand > m_run + kLazyLog2;  // first block: m_run = -inf
+    const bool grow = cand > m_run + kLazyLog2;
     if (__any(grow)) {
       const float m_new = grow ? cand : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first block, 1 where kept
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first tile, 1 where kept
       m_run = m_new;
 #pragma unroll
       for (int t = 0; t < 3; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
     }
-
+    // one basic block: exp of stage it, S^T of stage it + 1 (its buffer is
+    // published, or unused data past the last stage), P.V of stage it
+    bf16x8 pb[2];
 #pragma unroll
-    for (int sb = 0; sb < SB; ++sb)
+    for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        bf16x8 pb;
+      for (int e = 0; e < 8; ++e)
+        pb[s2][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s_cur[8 * s2 + e], scale_log2, -m_run));
+    QV_ATTN_S(it + 1, s_nxt)
+    const uint16_t* sV = reinterpret_cast<const uint16_t*>(lds + (it % NST) * STAGE_BYTES + K_SLOTS * 16);
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          pb[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[sb][8 * s2 + e], scale_log2, -m_run));
-        const int chunk = 4 * sb + 2 * s2 + hlf;
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int chunk = 4 * kw + 2 * s2 + hlf;  // 8-key chunk of the stage's IK keys
 #pragma unroll
-        for (int t = 0; t < 3; ++t) {
-          const int d = 32 * t + l32;
-          bf16x8 vf;
-          if (t < 2 || l32 < kHeadDim - 64)
-            vf = *reinterpret_cast<const bf16x8*>(&sV[(kw * kHeadDim + d) * KT + (v_swz<KT>(d, chunk) << 3)]);
-          else
-            vf = vconst;
-          o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, o[t], 0, 0, 0);
-        }
+      for (int t = 0; t < 3; ++t) {
+        const int d = 32 * t + l32;
+        bf16x8 vf;
+        if (t < 2 || l32 < kHeadDim - 64)
+          vf = *reinterpret_cast<const bf16x8*>(sV + d * IK + (v_swz<IK>(d, chunk) << 3));
+        else
+          vf = vconst;
+        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[s2], o[t], 0, 0, 0);
       }
+    }
+    s_cur = s_nxt;
   }
+#undef QV_ATTN_S
+#undef QV_ATTN_MASK
+#undef QV_ATTN_ISSUE
 
   if constexpr (KW > 1) {
     // combine the KW key groups of each query group: O = sum_w 2^(m_w - M) O_w
     float* comb = reinterpret_cast<float*>(lds);
-    __syncthreads();
+    QV_BARRIER();  // every wave is done with the ring (all its loads were waited for)
     if (kw > 0) {
       float* dst = comb + ((kw - 1) * QW + qw) * 49 * 64;
 #pragma unroll
@@ -284,26 +324,22 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a, float scale_log2)
         }
       }
   }
-#undef QV_ATTN_GLOAD
-#undef QV_ATTN_SSTORE
 }
 
 int attention_bf16_rows_per_wg(int64_t wgs_at_128) {
-  // enough workgroups for two per CU: split keys across waves when the
-  // 128-row tiling leaves the GPU under-filled
-  if (wgs_at_128 >= 512) return 128;
-  if (wgs_at_128 * 2 >= 512) return 64;
-  return 32;
+  // 128 query rows per workgroup when that alone gives a workgroup per CU,
+  // else 64 (the key split doubles the workgroups)
+  return wgs_at_128 >= 256 ? 128 : 64;
 }
 
 hipError_t attention_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.total_qtiles == 0) return hipSuccess;
+  if (a.P % 128) return hipErrorInvalidValue;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)kHeadDim);
   const dim3 grid((unsigned)a.total_qtiles * (unsigned)a.heads);
   switch (a.rows_per_wg) {
-    case 128: hipLaunchKernelGGL((k_attn_bf16<1, 64>), grid, dim3(256), 0, s, a, scale_log2); break;
-    case 64: hipLaunchKernelGGL((k_attn_bf16<2, 32>), grid, dim3(256), 0, s, a, scale_log2); break;
-    case 32: hipLaunchKernelGGL((k_attn_bf16<4, 32>), grid, dim3(256), 0, s, a, scale_log2); break;
+    case 128: hipLaunchKernelGGL((k_attn_bf16<4, 2>), grid, dim3(512), 0, s, a, scale_log2); break;
+    case 64: hipLaunchKernelGGL((k_attn_bf16<2, 4>), grid, dim3(512), 0, s, a, scale_log2); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -323,7 +323,8 @@ struct EpiQkv {
           }
 #pragma unroll
         for (int fp = 0; fp < NP; ++fp) {
-          uint16_t* base = reinterpret_cast<uint16_t*>(wn0 + fp * 64 >= dim ? o.k : o.q);
+          const bool isk = wn0 + fp * 64 >= dim;
+          uint16_t* base = reinterpret_cast<uint16_t*>(isk ? o.k : o.q);
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int rl = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -346,7 +347,9 @@ struct EpiQkv {
               pk.y = pack_bf16(a0.z, a0.w);
               pk.z = pack_bf16(a1.x, a1.y);
               pk.w = pack_bf16(a1.z, a1.w);
-              const size_t off = ((size_t)hd * o.P + prow[pass]) * kHeadDim + j0 + h * (kHeadDim / 2);
+              const int d0 = j0 + h * (kHeadDim / 2);  // 8 consecutive dims, one 16-byte chunk
+              const size_t off = isk ? kc_offset(hd, o.P, prow[pass], d0)
+                                     : ((size_t)hd * o.P + prow[pass]) * kHeadDim + d0;
               *reinterpret_cast<uint4*>(base + off) = pk;
             }
           }
@@ -408,7 +411,8 @@ struct EpiQkv {
         const int head = pair / (kHeadDim / 2), j = pair % (kHeadDim / 2);
         const int f0 = region * dim + head * kHeadDim + j;
         const float b0 = bias[f0], b1 = bias[f0 + kHeadDim / 2];
-        uint16_t* dst = reinterpret_cast<uint16_t*>(region ? o.k : o.q) + (size_t)head * o.P * kHeadDim + j;
+        uint16_t* qdst = reinterpret_cast<uint16_t*>(o.q) + (size_t)head * o.P * kHeadDim + j;
+        uint16_t* kdst = reinterpret_cast<uint16_t*>(o.k);
         const int fi = j < kRopeFreqs ? j : j - kRopeFreqs;
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
@@ -420,9 +424,15 @@ struct EpiQkv {
             const int p = j < kRopeFreqs ? (ti.x & 0xFFFF) : (ti.x >> 16);
             const float2 cs = o.rope[p * kRopeFreqs + fi];
             const float x0 = acc[fm][fp][r] + b0, x1 = acc[fm][fp + 1][r] + b1;
-            uint16_t* d = dst + (size_t)ti.y * kHeadDim;
-            d[0] = bf16_bits(x0 * cs.x - x1 * cs.y);
-            d[kHeadDim / 2] = bf16_bits(x1 * cs.x + x0 * cs.y);
+            const uint16_t y0 = bf16_bits(x0 * cs.x - x1 * cs.y), y1 = bf16_bits(x1 * cs.x + x0 * cs.y);
+            if (region) {
+              kdst[kc_offset(head, o.P, ti.y, j)] = y0;
+              kdst[kc_offset(head, o.P, ti.y, j + kHeadDim / 2)] = y1;
+            } else {
+              uint16_t* d = qdst + (size_t)ti.y * kHeadDim;
+              d[0] = y0;
+              d[kHeadDim / 2] = y1;
+            }
           }
       }
     } else {

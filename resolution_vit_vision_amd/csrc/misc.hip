@@ -151,32 +151,35 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
 }
 
 // ------------------------------------------------------------ cache warm-up
-// Reads `bytes` of `src` (16-byte multiple) so that they pass through L2 and
-// stay in the Infinity Cache for a kernel that runs a little later on another
+// Reads `n16` 16-byte words of `src` so that they pass through L2 and stay in
+// the Infinity Cache for a kernel that runs a little later on another
 // stream: the GEMMs stream their weights once per forward, and a cold weight
 // panel costs them HBM latency they cannot hide in LDS.  One wave per
-// workgroup, LDS-DMA into a 1 KB sink (nothing is kept or waited on per
-// load), at most 24 loads in flight per wave; the wave drains its loads
-// before it ends so no DMA write can land in LDS the workgroup no longer owns.
-#define QV_WARM_WAIT_VM(n) \
-  __builtin_amdgcn_s_waitcnt(((n) & 0xF) | 0x70 | 0xF00 | ((((n) >> 4) & 3) << 14))
-__global__ __launch_bounds__(64) void k_warm(const char* __restrict__ src, size_t bytes) {
-  __shared__ __attribute__((aligned(1024))) char sink[1024];
-  typedef const __attribute__((address_space(1))) void* gas_ptr;
-  typedef __attribute__((address_space(3))) void* las_ptr;
-  const int lane = threadIdx.x;
-  int n = 0;
-  for (size_t off = (size_t)blockIdx.x * 1024; off < bytes; off += (size_t)gridDim.x * 1024) {
-    const size_t at = off + (size_t)lane * 16;
-    if (at < bytes) __builtin_amdgcn_global_load_lds((gas_ptr)(src + at), (las_ptr)sink, 16, 0, 0);
-    if (++n >= 24) QV_WARM_WAIT_VM(23);
+// workgroup, no LDS (so a warm-up wave never keeps an LDS-hungry workgroup
+// off a CU), 16 loads of 16 bytes in flight per lane.  The words are folded
+// into a value that is stored only if it equals a constant, which keeps the
+// loads without writing anything in practice.
+__device__ uint32_t g_warm_sink[64];
+
+__global__ __launch_bounds__(64) void k_warm(const uint4* __restrict__ src, size_t n16) {
+  constexpr int U = 16;
+  const size_t stride = (size_t)gridDim.x * 64;
+  size_t i = (size_t)blockIdx.x * 64 + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + (U - 1) * stride < n16; i += U * stride) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = src[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].w;
   }
-  QV_WARM_WAIT_VM(0);
+  for (; i < n16; i += stride) acc ^= src[i].x;
+  if (acc == 0x9E3779B9u) g_warm_sink[threadIdx.x] = acc;
 }
 
 hipError_t launch_warm(const void* src, size_t bytes, hipStream_t s) {
   if (!src || bytes < 16) return hipSuccess;
-  hipLaunchKernelGGL(k_warm, dim3(64), dim3(64), 0, s, reinterpret_cast<const char*>(src), bytes & ~(size_t)15);
+  hipLaunchKernelGGL(k_warm, dim3(256), dim3(64), 0, s, reinterpret_cast<const uint4*>(src), bytes / 16);
   return hipGetLastError();
 }
 

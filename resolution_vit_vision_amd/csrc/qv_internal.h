@@ -62,10 +62,19 @@ hipError_t launch_warm(const void* src, size_t bytes, hipStream_t s);
 hipError_t launch_layernorm(const float* x, const float* g, const float* b, void* y, bool bf16, int rows,
                             int dim, float eps, hipStream_t s);
 
+// K of the bf16 path is stored key-tiled and chunk-major per head:
+// [head][P / 32][10 chunks of 8 dims][32 keys][8 dims], so the 32 key rows an
+// attention wave multiplies are, chunk by chunk, 32 consecutive 16-byte slots
+// (conflict-free LDS reads), and a run of keys is one contiguous block of
+// memory (whole-KB LDS-DMA copies).  Element offset of (head, key, dim):
+__host__ __device__ __forceinline__ size_t kc_offset(int head, int P, int key, int d) {
+  return ((((size_t)head * (P / 32) + (key >> 5)) * (kHeadDim / 8) + (d >> 3)) * 32 + (key & 31)) * 8 + (d & 7);
+}
+
 // C = A . B^T with an epilogue (bf16 operands, MFMA).
 struct QkvOut {
   void* q;         // [heads][P][80]
-  void* k;         // [heads][P][80]
+  void* k;         // bf16: key-tiled (kc_offset); f32: [heads][P][80]
   void* vt;        // [heads][80][P]
   const int2* tokinfo;
   const float2* rope;  // [positions][20] (cos, sin)
