@@ -4,11 +4,8 @@
 
 namespace qv {
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
+// float -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 // ------------------------------------------------------------------ patchify
 // One thread writes 8 consecutive elements of one output row.  Rows of an
@@ -196,13 +193,20 @@ __global__ __launch_bounds__(256) void k_layernorm(const float* __restrict__ x, 
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
   const float4* xr = reinterpret_cast<const float4*>(x + (size_t)row * D);
-  float4 v[NV];
-  float sum = 0.f;
+  const float4* g4 = reinterpret_cast<const float4*>(g);
+  const float4* b4 = reinterpret_cast<const float4*>(b);
+  float4 v[NV], gg[NV], bb[NV];
+  // every load (row, gain, bias) issued up front: one memory round trip
+#pragma unroll
+  for (int i = 0; i < NV; ++i) v[i] = xr[i * 64 + lane];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    v[i] = xr[i * 64 + lane];
-    sum += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+    gg[i] = g4[i * 64 + lane];
+    bb[i] = b4[i * 64 + lane];
   }
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) sum += (v[i].x + v[i].y) + (v[i].z + v[i].w);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
   const float mean = sum * (1.0f / D);
@@ -215,13 +219,10 @@ __global__ __launch_bounds__(256) void k_layernorm(const float* __restrict__ x, 
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
   const float rstd = rsqrtf(sq * (1.0f / D) + eps);
-  const float4* g4 = reinterpret_cast<const float4*>(g);
-  const float4* b4 = reinterpret_cast<const float4*>(b);
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const float4 gg = g4[i * 64 + lane], bb = b4[i * 64 + lane];
-    const float o0 = v[i].x * rstd * gg.x + bb.x, o1 = v[i].y * rstd * gg.y + bb.y;
-    const float o2 = v[i].z * rstd * gg.z + bb.z, o3 = v[i].w * rstd * gg.w + bb.w;
+    const float o0 = v[i].x * rstd * gg[i].x + bb[i].x, o1 = v[i].y * rstd * gg[i].y + bb[i].y;
+    const float o2 = v[i].z * rstd * gg[i].z + bb[i].z, o3 = v[i].w * rstd * gg[i].w + bb[i].w;
     if (bf16) {
       uint2 pk;
       pk.x = f32_to_bf16_rne(o0) | ((uint32_t)f32_to_bf16_rne(o1) << 16);
