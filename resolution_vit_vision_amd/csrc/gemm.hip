@@ -120,7 +120,8 @@ __device__ __forceinline__ void staged_store(const Op& op, f32x16 (&acc)[FM][FN]
 // QuickGELU for the bf16 path with a hardware reciprocal (1 ulp; the result
 // is rounded to bf16).
 __device__ __forceinline__ float act_apply_fast(Act a, float u) {
-  if (a == Act::QuickGelu) return u * __builtin_amdgcn_rcpf(1.0f + __expf(-1.702f * u));
+  // sigma(1.702 u) = 1 / (1 + 2^(-1.702 log2(e) u)); v_exp_f32 and v_rcp_f32
+  if (a == Act::QuickGelu) return u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-2.4554669595930157f * u));
   return act_apply(a, u);
 }
 
@@ -198,14 +199,17 @@ struct EpiResidF32 {
   }
 };
 
+// The activation is a template parameter: a run-time switch compiled every
+// activation (erf included) into each element's path.
+template <Act ACT>
 struct EpiActBf16 {
   static constexpr bool kStaged = true;
   static constexpr int kPatchFloats = 32 * 40;
   using RowParam = NoRowParam;
   static constexpr int kRowParamFloats = 0;
-  uint16_t* C; int ldc; const float* bias; Act act;
+  uint16_t* C; int ldc; const float* bias;
   __device__ float col_param(int col) const { return bias[col]; }
-  __device__ float pre(float cp, float v) const { return act_apply_fast(act, v + cp); }
+  __device__ float pre(float cp, float v) const { return act_apply_fast(ACT, v + cp); }
   __device__ RowParam row_param(int, int) const { return {}; }
   __device__ void store(int row, int col, const float (&v)[8], const RowParam&) const {
     uint4 pk;
@@ -663,8 +667,15 @@ hipError_t gemm_bf16_resid_f32(const void* A, int lda, const void* B, int ldb, i
 }
 hipError_t gemm_bf16_act_bf16(const void* A, int lda, const void* B, int ldb, int M, int N, int K,
                               const float* bias, Act act, void* C, int ldc, hipStream_t s) {
-  return run_bf16(A, lda, B, ldb, M, N, K, EpiActBf16{reinterpret_cast<uint16_t*>(C), ldc, bias, act},
-                  RowMapIdentity{}, s);
+  uint16_t* c = reinterpret_cast<uint16_t*>(C);
+  switch (act) {
+    case Act::QuickGelu:
+      return run_bf16(A, lda, B, ldb, M, N, K, EpiActBf16<Act::QuickGelu>{c, ldc, bias}, RowMapIdentity{}, s);
+    case Act::GeluErf:
+      return run_bf16(A, lda, B, ldb, M, N, K, EpiActBf16<Act::GeluErf>{c, ldc, bias}, RowMapIdentity{}, s);
+    default:
+      return run_bf16(A, lda, B, ldb, M, N, K, EpiActBf16<Act::None>{c, ldc, bias}, RowMapIdentity{}, s);
+  }
 }
 hipError_t gemm_bf16_qkv(const void* A, int lda, const void* B, int ldb, int M, int K, const float* bias,
                          const QkvOut& o, hipStream_t s) {
