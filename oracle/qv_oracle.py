@@ -29,6 +29,10 @@ title and section):
   attention   full bidirectional attention inside each image of a packed
               batch (block-diagonal by cu_seqlens) [LiteRT-LM card,
               Conversion notes]
+  windows     optional windowed attention (Qwen2.5-VL style): attention
+              inside windows of `window` x `window` patches except in the
+              listed full-attention blocks [Qwen2.5-VL-7B-Instruct record,
+              TWO-PART MODEL]
   merge       LayerNorm -> 4 consecutive tokens concatenated (5120) ->
               Linear -> GELU -> Linear to the decoder width
               [Neurarch card, Exported PyTorch: PatchMerger; LiteRT-LM
@@ -283,6 +287,55 @@ def attention_varlen(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_seqlens: np
     return out
 
 
+# --------------------------------------------------------- windowed attention
+def window_groups(grids: Sequence[Tuple[int, int, int]], window: int, merge: int = MERGE) -> List[np.ndarray]:
+    """Token index lists (packed rows) of the attention windows of a batch.
+
+    The Qwen2.5-VL record keeps the Qwen2-VL tower shapes but lets attention
+    run inside windows of 112 px = 8 x 8 patches, with only four blocks
+    attending over the whole image [Qwen2.5-VL-7B-Instruct record, TWO-PART
+    MODEL].  Readings (the record says nothing more): windows tile each
+    frame's patch grid from its top-left corner in steps of ``window``
+    patches; a window at the right or bottom edge holds only the patches
+    that exist (no padding token takes part); each frame of an image has its
+    own windows; a window's tokens keep their packed order.  Windows are
+    listed image by image, frame by frame, in raster order."""
+    if window <= 0 or window % merge:
+        raise ValueError("window must be a positive multiple of the merge size")
+    cu, pos, _ = seq_meta(grids, merge)
+    groups: List[np.ndarray] = []
+    for i, (t, gh, gw) in enumerate(grids):
+        nwx = (gw + window - 1) // window
+        nwy = (gh + window - 1) // window
+        for tt in range(t):
+            rows = np.arange(cu[i] + tt * gh * gw, cu[i] + (tt + 1) * gh * gw)
+            key = (pos[rows, 0] // window) * nwx + pos[rows, 1] // window
+            for wk in range(nwy * nwx):
+                groups.append(rows[key == wk])
+    return groups
+
+
+def attention_groups(q: np.ndarray, k: np.ndarray, v: np.ndarray, groups: Sequence[np.ndarray]) -> np.ndarray:
+    """Attention inside each group of rows (any row subset, e.g. a window):
+    for every group and head, softmax(q k^T / sqrt(hd)) v over the group's
+    own keys, row max subtracted.  Rows outside every group stay zero."""
+    n, heads, hd = q.shape
+    scale = 1.0 / math.sqrt(hd)
+    out = np.zeros_like(q)
+
+    def run(g):
+        for h in range(heads):
+            s = (q[g, h, :] @ k[g, h, :].T) * scale
+            s = s - s.max(axis=1, keepdims=True)
+            p = np.exp(s)
+            p /= p.sum(axis=1, keepdims=True)
+            out[g, h, :] = p @ v[g, h, :]
+
+    with ThreadPoolExecutor(max_workers=_threads()) as ex:
+        list(ex.map(run, groups))
+    return out
+
+
 # ------------------------------------------------------------------- the tower
 def patch_embed(x: np.ndarray, w: np.ndarray, b: np.ndarray | None = None) -> np.ndarray:
     """Conv3d with kernel = stride = (2, 14, 14) on non-overlapping patches is
@@ -294,11 +347,13 @@ def patch_embed(x: np.ndarray, w: np.ndarray, b: np.ndarray | None = None) -> np
 
 
 def vision_block(z: np.ndarray, p: Dict[str, np.ndarray], cu_seqlens: np.ndarray,
-                 angles: np.ndarray, heads: int = 16, eps: float = 1e-6) -> np.ndarray:
+                 angles: np.ndarray, heads: int = 16, eps: float = 1e-6,
+                 groups: Sequence[np.ndarray] | None = None) -> np.ndarray:
     """One pre-norm rotary ViT block on the packed residual stream z [N][d].
 
       a = LN1(z); [q|k|v] = a Wqkv^T + b (q, k, v each head-major);
-      q, k rotated by the 2-D rope; o = attention per image;
+      q, k rotated by the 2-D rope; o = attention per image (or per
+      window when ``groups`` lists the windows);
       z = z + o Wo^T + bo; a = LN2(z); z = z + QuickGELU(a W1^T + b1) W2^T + b2.
     Reading: pre-norm with biases on every Linear, QuickGELU, eps 1e-6, scale
     1/sqrt(hd) (the workloads' definition; the pages' generic exported
@@ -312,7 +367,10 @@ def vision_block(z: np.ndarray, p: Dict[str, np.ndarray], cu_seqlens: np.ndarray
     v = qkv[:, 2 * d:3 * d].reshape(n, heads, hd)
     q = apply_rope(q, angles)
     k = apply_rope(k, angles)
-    o = attention_varlen(q, k, v, cu_seqlens).reshape(n, d)
+    if groups is None:
+        o = attention_varlen(q, k, v, cu_seqlens).reshape(n, d)
+    else:  # a windowed block: attention inside each window only
+        o = attention_groups(q, k, v, groups).reshape(n, d)
     z = z + o @ p["proj_w"].T + p["proj_b"]
     a = layer_norm(z, p["ln2_w"], p["ln2_b"], eps)
     return z + quick_gelu(a @ p["fc1_w"].T + p["fc1_b"]) @ p["fc2_w"].T + p["fc2_b"]
@@ -358,19 +416,24 @@ def block_params(params: Dict[str, np.ndarray], l: int, dtype=np.float64) -> Dic
 
 def vision_forward(x: np.ndarray, params: Dict[str, np.ndarray], grids, depth: int,
                    heads: int = 16, eps: float = 1e-6, theta: float = 1e4,
-                   dtype=np.float64, return_all: bool = False):
+                   dtype=np.float64, return_all: bool = False, window: int = 0,
+                   full_blocks: Sequence[int] = ()):
     """Patch-embed, then ``depth`` rotary blocks over the packed images
     [ZeroModels docs, Qwen2VLVisionModel: patch-embed -> rotary blocks ->
     merger].  Returns the residual stream [N][d] before the merger (the
     encoder output of the LiteRT-LM card's VISION_ENCODER); with
-    ``return_all`` also every block's input."""
+    ``return_all`` also every block's input.  ``window`` > 0 makes every
+    block not listed in ``full_blocks`` attend inside windows of that many
+    patches (``window_groups``)."""
     cu, pos, _ = seq_meta(grids)
     d = params["patch_w"].shape[0]
     angles = rope_angles(pos, d // heads, theta)
+    groups = window_groups(grids, window) if window else None
     z = patch_embed(x.astype(dtype), params["patch_w"].astype(dtype))
     states = [z]
     for l in range(depth):
-        z = vision_block(z, block_params(params, l, dtype), cu, angles, heads, eps)
+        g = groups if (groups is not None and l not in full_blocks) else None
+        z = vision_block(z, block_params(params, l, dtype), cu, angles, heads, eps, groups=g)
         states.append(z)
     return (z, states) if return_all else z
 
@@ -396,7 +459,8 @@ def patch_merge(z: np.ndarray, params: Dict[str, np.ndarray], merge: int = MERGE
 
 def encode(images: Sequence[np.ndarray], params: Dict[str, np.ndarray], depth: int,
            heads: int = 16, eps: float = 1e-6, theta: float = 1e4, dtype=np.float64,
-           min_pixels: int = MIN_PIXELS, max_pixels: int = MAX_PIXELS):
+           min_pixels: int = MIN_PIXELS, max_pixels: int = MAX_PIXELS, window: int = 0,
+           full_blocks: Sequence[int] = ()):
     """Whole path for images whose sides already sit on the grid:
     grid -> patchify -> tower -> merger.  Returns (grids, hidden, merged)."""
     grids = []
@@ -407,5 +471,5 @@ def encode(images: Sequence[np.ndarray], params: Dict[str, np.ndarray], depth: i
             raise ValueError("image sides must already be multiples of 28 inside the budget")
         grids.append(g)
     x = patchify(images, grids)
-    z = vision_forward(x, params, grids, depth, heads, eps, theta, dtype)
+    z = vision_forward(x, params, grids, depth, heads, eps, theta, dtype, window=window, full_blocks=full_blocks)
     return grids, z, patch_merge(z, params, eps=eps, dtype=dtype)

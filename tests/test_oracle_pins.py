@@ -484,3 +484,116 @@ def test_tower_depth_zero_is_patch_embed():
     z = O.vision_forward(O.patchify([img], [g]), {"patch_w": w}, [g], depth=0, heads=3)
     _, _, perm = O.seq_meta([g])
     np.testing.assert_allclose(z, _conv3d_reference(img, w)[perm], rtol=1e-12)
+
+
+# ------------------------------------------------------------ windowed attention
+def test_window_groups_hand_listed():
+    """window_groups on a 4 x 6 grid with 4-patch windows, listed by hand from
+    the merge-group order (groups (0,0) (0,1) (0,2) / (1,0) (1,1) (1,2), four
+    slots each): the left window holds groups (0,0) (0,1) (1,0) (1,1), the
+    truncated right window groups (0,2) (1,2).  A swapped h/w or a window
+    key without the row term fails here."""
+    got = [list(map(int, g)) for g in O.window_groups([(1, 4, 6)], 4)]
+    assert got == [list(range(0, 8)) + list(range(12, 20)), list(range(8, 12)) + list(range(20, 24))]
+
+
+@pytest.mark.parametrize("grids,window", [([(1, 10, 10)], 4), ([(1, 8, 8), (1, 6, 14)], 4),
+                                          ([(2, 6, 4)], 2), ([(1, 16, 12)], 8)])
+def test_window_groups_partition(grids, window):
+    """Windows partition each frame; sizes follow min(W, edge remainder) on
+    both axes; all members of a window share (image, frame, h // W, w // W)."""
+    cu, pos, _ = O.seq_meta(grids)
+    groups = O.window_groups(grids, window)
+    allrows = np.sort(np.concatenate(groups))
+    np.testing.assert_array_equal(allrows, np.arange(cu[-1]))
+    gi = 0
+    for i, (t, gh, gw) in enumerate(grids):
+        for tt in range(t):
+            for wy in range(-(-gh // window)):
+                for wx in range(-(-gw // window)):
+                    g = groups[gi]
+                    gi += 1
+                    assert len(g) == min(window, gh - wy * window) * min(window, gw - wx * window)
+                    assert np.all((g >= cu[i] + tt * gh * gw) & (g < cu[i] + (tt + 1) * gh * gw))
+                    assert np.all(pos[g, 0] // window == wy) and np.all(pos[g, 1] // window == wx)
+    assert gi == len(groups)
+
+
+def _brute_masked_attention(q, k, v, same):
+    n, heads, hd = q.shape
+    out = np.zeros_like(q)
+    for h in range(heads):
+        for a in range(n):
+            js = [b for b in range(n) if same(a, b)]
+            s = [sum(q[a, h, d] * k[b, h, d] for d in range(hd)) / math.sqrt(hd) for b in js]
+            m = max(s)
+            e = [math.exp(x - m) for x in s]
+            z = sum(e)
+            for d in range(hd):
+                out[a, h, d] = sum(e[j] * v[b, h, d] for j, b in enumerate(js)) / z
+    return out
+
+
+def test_window_attention_bruteforce():
+    """attention_groups over the windows of a 6 x 6 grid (W = 4: windows of
+    16, 8, 8 and 4 patches) equals a masked triple loop where a attends b
+    iff both sit in the same window (h // 4, w // 4)."""
+    grids = [(1, 6, 6)]
+    _, pos, _ = O.seq_meta(grids)
+    rng = np.random.default_rng(11)
+    q, k, v = (rng.standard_normal((36, 2, 4)) for _ in range(3))
+    got = O.attention_groups(q, k, v, O.window_groups(grids, 4))
+    same = lambda a, b: (pos[a, 0] // 4, pos[a, 1] // 4) == (pos[b, 0] // 4, pos[b, 1] // 4)
+    np.testing.assert_allclose(got, _brute_masked_attention(q, k, v, same), rtol=1e-12, atol=1e-12)
+
+
+def _tiny_tower_params(d=64, heads=4, mlp=128, depth=2, seed=3):
+    rng = np.random.default_rng(seed)
+    p = {"patch_w": rng.standard_normal((d, 3 * 2 * 14 * 14)) * 0.02}
+    for l in range(depth):
+        pre = f"blocks.{l}."
+        p[pre + "ln1_w"] = 1 + rng.standard_normal(d) * 0.02
+        p[pre + "ln1_b"] = rng.standard_normal(d) * 0.02
+        p[pre + "qkv_w"] = rng.standard_normal((3 * d, d)) * 0.2
+        p[pre + "qkv_b"] = rng.standard_normal(3 * d) * 0.02
+        p[pre + "proj_w"] = rng.standard_normal((d, d)) * 0.2
+        p[pre + "proj_b"] = rng.standard_normal(d) * 0.02
+        p[pre + "ln2_w"] = 1 + rng.standard_normal(d) * 0.02
+        p[pre + "ln2_b"] = rng.standard_normal(d) * 0.02
+        p[pre + "fc1_w"] = rng.standard_normal((mlp, d)) * 0.2
+        p[pre + "fc1_b"] = rng.standard_normal(mlp) * 0.02
+        p[pre + "fc2_w"] = rng.standard_normal((d, mlp)) * 0.2
+        p[pre + "fc2_b"] = rng.standard_normal(d) * 0.02
+    return p
+
+
+def test_windowed_tower_special_cases():
+    """A window covering the whole grid, or every block listed as full, gives
+    the unwindowed tower; a real window changes the result."""
+    grids = [(1, 6, 8), (1, 4, 4)]
+    p = _tiny_tower_params()
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((48 + 16, 3 * 2 * 14 * 14))
+    full = O.vision_forward(x, p, grids, 2, heads=4)
+    np.testing.assert_allclose(O.vision_forward(x, p, grids, 2, heads=4, window=8), full, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(O.vision_forward(x, p, grids, 2, heads=4, window=2, full_blocks=(0, 1)), full,
+                               rtol=1e-12, atol=1e-12)
+    assert not np.allclose(O.vision_forward(x, p, grids, 2, heads=4, window=2), full, rtol=1e-6)
+
+
+def test_windowed_block_isolates_windows():
+    """In a windowed block, changing the input rows of one window changes the
+    output rows of that window only (LayerNorm and the MLP are per row)."""
+    grids = [(1, 8, 8)]
+    cu, pos, _ = O.seq_meta(grids)
+    p = O.block_params(_tiny_tower_params(depth=1), 0)
+    angles = O.rope_angles(pos, 16)
+    groups = O.window_groups(grids, 4)
+    rng = np.random.default_rng(9)
+    z = rng.standard_normal((64, 64))
+    base = O.vision_block(z, p, cu, angles, heads=4, groups=groups)
+    z2 = z.copy()
+    z2[groups[1]] += rng.standard_normal((len(groups[1]), 64))
+    out = O.vision_block(z2, p, cu, angles, heads=4, groups=groups)
+    changed = np.nonzero(np.any(np.abs(out - base) > 0, axis=1))[0]
+    np.testing.assert_array_equal(np.sort(changed), np.sort(groups[1]))
