@@ -32,14 +32,26 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 def workload_flops(wl, grids):
     """Algorithmic FLOPs of one step: true K (1176), block-diagonal attention
-    (sum n_i^2), matrix products only."""
+    (sum n_i^2 over images, or over windows in the windowed blocks), matrix
+    products only.  "attention" is the average over the step's blocks."""
     ns = [t * gh * gw for t, gh, gw in grids]
     n, m = sum(ns), sum(ns) // 4
     d, f, pd, hid = wl.dim, wl.mlp, wl.patch_dim, wl.merged_dim
+    att_full = 4 * d * sum(x * x for x in ns)
+    att = att_full
+    if wl.window and wl.depth:
+        W = wl.window
+        sq = 0
+        for t, gh, gw in grids:
+            rows = [min(W, gh - y) for y in range(0, gh, W)]
+            cols = [min(W, gw - x) for x in range(0, gw, W)]
+            sq += t * sum((r * c) ** 2 for r in rows for c in cols)
+        nfull = sum(1 for b in wl.full_blocks if b < wl.depth)
+        att = (nfull * att_full + (wl.depth - nfull) * 4 * d * sq) / wl.depth
     per = {
         "patch_embed": 2 * n * pd * d,
         "qkv": 2 * n * d * 3 * d,
-        "attention": 4 * d * sum(x * x for x in ns),
+        "attention": att,
         "proj": 2 * n * d * d,
         "fc1": 2 * n * d * f,
         "fc2": 2 * n * f * d,
@@ -86,7 +98,7 @@ def cpu_baseline(wl, params, imgs):
         blas_threads = None
     cores = len(os.sched_getaffinity(0))
     t0 = time.perf_counter()
-    grids, z, out = O.encode(imgs, params, depth=wl.depth)
+    grids, z, out = O.encode(imgs, params, depth=wl.depth, window=wl.window, full_blocks=wl.full_blocks)
     dt = time.perf_counter() - t0
     m = out.shape[0]
     return {"value": m / dt, "unit": "tokens/s", "cores": max(cores, blas_threads or 1), "kind": "oracle",
@@ -139,7 +151,8 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     params = synth.params(wl)
     imgs = synth.pixels(wl)
-    enc = qv.Encoder(params, imgs, depth=wl.depth, out_dim=wl.out_dim, dtype=wl.dtype)
+    enc = qv.Encoder(params, imgs, depth=wl.depth, out_dim=wl.out_dim, dtype=wl.dtype, window=wl.window,
+                     full_blocks=wl.full_blocks)
     grids = enc.grids
     n = enc.n
     m = n // 4
@@ -216,7 +229,7 @@ def main():
         "config": {"workload": wl.name, "images": [f"{h}x{w}" for h, w, _ in wl.images][:4]
                    + (["..."] if len(wl.images) > 4 else []),
                    "n_images": len(wl.images), "patches": n, "merged_tokens": m, "depth": wl.depth,
-                   "out_dim": wl.out_dim},
+                   "out_dim": wl.out_dim, "window": wl.window, "full_blocks": list(wl.full_blocks)},
         "patches_per_s": n * args.steps / (ms / 1e3),
         "algorithmic_tflop_per_step": flops / 1e12,
         "achieved_tflops": flops / (ms_per_step / 1e3) / 1e12,

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define QV_ABI_VERSION 1
+#define QV_ABI_VERSION 2
 
 typedef enum qv_status {
   QV_OK = 0,
@@ -176,6 +176,17 @@ typedef struct qv_vision_cfg {
   int32_t dtype;      /* qv_dtype                                               */
   float ln_eps;       /* 1e-6                                                   */
   float rope_theta;   /* 1e4                                                    */
+  /* Windowed attention (Qwen2.5-VL-7B-Instruct record, TWO-PART MODEL: 112-px
+   * windows, full attention only in four blocks).  window: side of a window
+   * in patches, a positive multiple of merge and at most 10 (8 = 112 px);
+   * windows tile each frame's patch grid from its top-left corner, edge
+   * windows are truncated; 0 = every block attends over the whole image
+   * (Qwen2-VL).  full_blocks: with window > 0, bit l set = block l attends
+   * over the whole image (Qwen2.5-VL: bits 7, 15, 23, 31); blocks from 64
+   * on are windowed.  full_blocks is ignored when window is 0. */
+  int32_t window;
+  int32_t reserved0;  /* 0 */
+  uint64_t full_blocks;
 } qv_vision_cfg;
 
 /* Bytes of device workspace qv_vision_forward needs for this grid list.
@@ -191,7 +202,8 @@ qv_status qv_vision_workspace_size(const qv_vision_cfg *c, const int32_t *grid_t
  *   a = LN1(hidden); [q|k|v] = a . qkv_w^T + qkv_b; q, k rotated by the 2-D
  *   rope of each patch's (h, w) (pair j couples elements j and j+40 of a
  *   head, pairs 0..19 turn by h * theta^(-j/20), pairs 20..39 by
- *   w * theta^(-(j-20)/20)); o = softmax(q k^T / sqrt(80)) v inside each image;
+ *   w * theta^(-(j-20)/20)); o = softmax(q k^T / sqrt(80)) v inside each image
+ *   (inside each window in the windowed blocks, see qv_vision_cfg.window);
  *   hidden += o . proj_w^T + proj_b; a = LN2(hidden);
  *   hidden += QuickGELU(a . fc1_w^T + fc1_b) . fc2_w^T + fc2_b.
  * patches: device [N][ld] in cfg dtype, merge-group order (qv_patchify).

@@ -378,20 +378,27 @@ def vision_block(z: np.ndarray, p: Dict[str, np.ndarray], cu_seqlens: np.ndarray
 
 def vision_block_rows(z: np.ndarray, p: Dict[str, np.ndarray], cu_seqlens: np.ndarray,
                       angles: np.ndarray, rows: np.ndarray, heads: int = 16,
-                      eps: float = 1e-6) -> np.ndarray:
+                      eps: float = 1e-6, groups: Sequence[np.ndarray] | None = None) -> np.ndarray:
     """The same block evaluated only at output rows ``rows``.
 
-    Keys and values are formed for every row of each image that holds a
-    requested row; queries, projection and MLP only for the requested
-    rows.  Identical arithmetic to ``vision_block`` restricted to those
-    outputs, for checks at sizes where the whole block is too slow."""
+    Keys and values are formed for every row of each image (or window, when
+    ``groups`` lists the windows) that holds a requested row; queries,
+    projection and MLP only for the requested rows.  Identical arithmetic to
+    ``vision_block`` restricted to those outputs, for checks at sizes where
+    the whole block is too slow."""
     n, d = z.shape
     hd = d // heads
     rows = np.asarray(rows)
-    seg = np.searchsorted(cu_seqlens, rows, side="right") - 1
-    imgs = np.unique(seg)
-    kv_rows = np.concatenate([np.arange(cu_seqlens[i], cu_seqlens[i + 1]) for i in imgs])
-    sub_cu = np.concatenate([[0], np.cumsum([cu_seqlens[i + 1] - cu_seqlens[i] for i in imgs])])
+    if groups is None:
+        groups = [np.arange(cu_seqlens[i], cu_seqlens[i + 1]) for i in range(len(cu_seqlens) - 1)]
+    owner = np.full(n, -1, dtype=np.int64)
+    for gi, g in enumerate(groups):
+        owner[g] = gi
+    used = np.unique(owner[rows])
+    if (used < 0).any():
+        raise ValueError("a requested row belongs to no attention group")
+    kv_rows = np.concatenate([groups[i] for i in used])
+    sub_cu = np.concatenate([[0], np.cumsum([len(groups[i]) for i in used])])
     a = layer_norm(z[kv_rows], p["ln1_w"], p["ln1_b"], eps)
     kv = a @ p["qkv_w"][d:].T + p["qkv_b"][d:]
     k = apply_rope(kv[:, :d].reshape(-1, heads, hd), angles[kv_rows])

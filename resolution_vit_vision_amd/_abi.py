@@ -9,7 +9,7 @@ from __future__ import annotations
 import ctypes
 import os
 import re
-from ctypes import POINTER, Structure, c_char_p, c_float, c_int32, c_int64, c_size_t, c_void_p
+from ctypes import POINTER, Structure, c_char_p, c_float, c_int32, c_int64, c_size_t, c_uint64, c_void_p
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqv.so")
@@ -52,7 +52,8 @@ class VisionW(Structure):
 class VisionCfg(Structure):
     _fields_ = [("depth", c_int32), ("dim", c_int32), ("heads", c_int32), ("mlp", c_int32),
                 ("patch_dim", c_int32), ("ld", c_int32), ("merge", c_int32), ("dtype", c_int32),
-                ("ln_eps", c_float), ("rope_theta", c_float)]
+                ("ln_eps", c_float), ("rope_theta", c_float), ("window", c_int32), ("reserved0", c_int32),
+                ("full_blocks", c_uint64)]
 
 
 class MergerCfg(Structure):

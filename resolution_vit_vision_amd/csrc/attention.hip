@@ -110,8 +110,8 @@ __global__ __launch_bounds__(512) void k_attn_bf16(AttnArgs a, float scale_log2)
     }
   }
   const PlanEntry pe = a.plan[find_plan(a.plan, a.n_img, gt)];
-  const int row0 = a.cu_seqlens[pe.img];
-  const int n = a.cu_seqlens[pe.img + 1] - row0;
+  const int row0 = a.out_row ? 0 : a.cu_seqlens[pe.seg];
+  const int n = a.out_row ? pe.n : a.cu_seqlens[pe.seg + 1] - row0;
   const int qbase = (gt - pe.qtile0) * BQ + qw * 32;
 
   const uint16_t* Qh = reinterpret_cast<const uint16_t*>(a.q) + (size_t)head * a.P * kHeadDim;
@@ -310,7 +310,8 @@ __global__ __launch_bounds__(512) void k_attn_bf16(AttnArgs a, float scale_log2)
   const float inv = 1.0f / lsum;
   const int q = qbase + l32;
   if (q < n) {
-    uint16_t* orow = reinterpret_cast<uint16_t*>(a.o) + (size_t)(row0 + q) * a.ldo + head * kHeadDim;
+    const int orow_i = a.out_row ? a.out_row[pe.prow0 + q] : row0 + q;
+    uint16_t* orow = reinterpret_cast<uint16_t*>(a.o) + (size_t)orow_i * a.ldo + head * kHeadDim;
 #pragma unroll
     for (int t = 0; t < 3; ++t)
 #pragma unroll
@@ -356,8 +357,8 @@ __global__ __launch_bounds__(64) void k_attn_f32(AttnArgs a, float scale) {
   const int lane = threadIdx.x;
   const int head = blockIdx.y, gt = blockIdx.x;
   const PlanEntry pe = a.plan[find_plan(a.plan, a.n_img, gt)];
-  const int row0 = a.cu_seqlens[pe.img];
-  const int n = a.cu_seqlens[pe.img + 1] - row0;
+  const int row0 = a.out_row ? 0 : a.cu_seqlens[pe.seg];
+  const int n = a.out_row ? pe.n : a.cu_seqlens[pe.seg + 1] - row0;
   const int q = (gt - pe.qtile0) * FBQ + lane;
   const float* Qh = reinterpret_cast<const float*>(a.q) + (size_t)head * a.P * kHeadDim;
   const float* Kh = reinterpret_cast<const float*>(a.k) + (size_t)head * a.P * kHeadDim;
@@ -402,7 +403,8 @@ __global__ __launch_bounds__(64) void k_attn_f32(AttnArgs a, float scale) {
     __syncthreads();
   }
   if (q < n) {
-    float* orow = reinterpret_cast<float*>(a.o) + (size_t)(row0 + q) * a.ldo + head * kHeadDim;
+    const int orow_i = a.out_row ? a.out_row[pe.prow0 + q] : row0 + q;
+    float* orow = reinterpret_cast<float*>(a.o) + (size_t)orow_i * a.ldo + head * kHeadDim;
     const float inv = 1.0f / l;
 #pragma unroll
     for (int d = 0; d < kHeadDim; ++d) orow[d] = acc[d] * inv;

@@ -273,8 +273,13 @@ struct VisionPlan {
   size_t es = 2;
   std::vector<ImgDesc> desc;
   std::vector<PlanEntry> plan;
+  // windowed attention: a second padded layout with one kSeqAlign-row slot per window
+  int window = 0;
+  int64_t n_win = 0, Pw = 0;
+  int total_qtiles_w = 0;
+  std::vector<PlanEntry> plan_w;
   size_t off_tok = 0, off_plan = 0, off_rope = 0, off_a = 0, off_q = 0, off_k = 0, off_vt = 0, off_vt_end = 0,
-         off_o = 0, off_h = 0, off_qkv = 0, total = 0;
+         off_o = 0, off_h = 0, off_qkv = 0, off_tokw = 0, off_outrow = 0, off_planw = 0, total = 0;
 };
 
 qv_status check_vision_cfg(const qv_vision_cfg* c) {
@@ -292,6 +297,9 @@ qv_status check_vision_cfg(const qv_vision_cfg* c) {
   if (c->ld < c->patch_dim || c->ld % 8) return fail(QV_ERR_SHAPE, "ld %d must be >= patch_dim and a multiple of 8", c->ld);
   if (c->merge != 2) return fail(QV_ERR_UNSUPPORTED, "only merge 2 is implemented");
   if (!(c->ln_eps >= 0.f) || !(c->rope_theta > 0.f)) return fail(QV_ERR_SHAPE, "ln_eps >= 0 and rope_theta > 0 required");
+  if (c->window < 0 || c->window % c->merge || c->window > 10)
+    return fail(QV_ERR_UNSUPPORTED, "window %d must be 0 or a multiple of merge %d in [2, 10]", c->window, c->merge);
+  if (c->reserved0 != 0) return fail(QV_ERR_SHAPE, "reserved0 must be 0");
   return QV_OK;
 }
 
@@ -311,7 +319,7 @@ qv_status make_plan(const qv_vision_cfg* c, const int32_t* grid_thw, int32_t n_i
   for (int i = 0; i < n_img; ++i) {
     if (g[i].gh > 65535 || g[i].gw > 65535) return fail(QV_ERR_UNSUPPORTED, "grid side above 65535");
     const int64_t n = (int64_t)g[i].t * g[i].gh * g[i].gw;
-    vp.desc[i] = ImgDesc{(int32_t)row, (int32_t)n, g[i].t, g[i].gh, g[i].gw, (int32_t)prow};
+    vp.desc[i] = ImgDesc{(int32_t)row, (int32_t)n, g[i].t, g[i].gh, g[i].gw, (int32_t)prow, 0, 0, 0};
     if (n % kSeqAlign) vp.padded = true;
     row += n;
     prow += round_up(n, kSeqAlign);
@@ -335,7 +343,40 @@ qv_status make_plan(const qv_vision_cfg* c, const int32_t* grid_thw, int32_t n_i
     qt += (int)((d.n + bq - 1) / bq);
   }
   vp.total_qtiles = qt;
-  const size_t N = (size_t)vp.N, P = (size_t)vp.P, es = vp.es;
+  if (c->window > 0) {
+    // windows of at most 10 x 10 patches fit one kSeqAlign-row slot; queries
+    // in tiles of 64 rows (the bf16 kernel's 64-row workgroups read 128-key
+    // stages, exactly one slot)
+    const int W = c->window;
+    vp.window = W;
+    std::vector<int> wn;  // window sizes in global window order
+    for (int i = 0; i < n_img; ++i) {
+      ImgDesc& d = vp.desc[i];
+      d.nwy = (d.gh + W - 1) / W;
+      d.nwx = (d.gw + W - 1) / W;
+      d.wbase = (int32_t)wn.size();
+      for (int t = 0; t < d.t; ++t)
+        for (int wy = 0; wy < d.nwy; ++wy)
+          for (int wx = 0; wx < d.nwx; ++wx)
+            wn.push_back(std::min(W, d.gh - wy * W) * std::min(W, d.gw - wx * W));
+    }
+    vp.n_win = (int64_t)wn.size();
+    vp.Pw = vp.n_win * kSeqAlign;
+    if (vp.Pw > INT32_MAX / 2) return fail(QV_ERR_SHAPE, "batch too large");
+    const int bqw = c->dtype == QV_BF16 ? 64 : kAttnBQ_f32;
+    std::vector<int> worder((size_t)vp.n_win);
+    for (int64_t i = 0; i < vp.n_win; ++i) worder[i] = (int)i;
+    std::stable_sort(worder.begin(), worder.end(), [&](int a, int b) { return wn[a] > wn[b]; });
+    vp.plan_w.resize((size_t)vp.n_win);
+    int qtw = 0;
+    for (int64_t k = 0; k < vp.n_win; ++k) {
+      const int wi = worder[k];
+      vp.plan_w[k] = PlanEntry{wi, wi * kSeqAlign, qtw, wn[wi]};
+      qtw += (wn[wi] + bqw - 1) / bqw;
+    }
+    vp.total_qtiles_w = qtw;
+  }
+  const size_t N = (size_t)vp.N, P = (size_t)std::max(vp.P, vp.Pw), es = vp.es;
   size_t o = 0;
   vp.off_tok = o;  o = align_up(o + N * sizeof(int2));
   vp.off_plan = o; o = align_up(o + (size_t)n_img * sizeof(PlanEntry));
@@ -349,6 +390,11 @@ qv_status make_plan(const qv_vision_cfg* c, const int32_t* grid_thw, int32_t n_i
   vp.off_h = o;    o = align_up(o + N * c->mlp * es);
   vp.off_qkv = o;
   if (c->dtype == QV_F32) o = align_up(o + N * 3 * c->dim * sizeof(float));
+  if (vp.window) {
+    vp.off_tokw = o;   o = align_up(o + N * sizeof(int2));
+    vp.off_outrow = o; o = align_up(o + (size_t)vp.Pw * sizeof(int32_t));
+    vp.off_planw = o;  o = align_up(o + (size_t)vp.n_win * sizeof(PlanEntry));
+  }
   vp.total = o;
   return QV_OK;
 }
@@ -411,7 +457,11 @@ qv_status qv_vision_forward(const qv_vision_cfg* c, const qv_vision_w* w, const 
   void* A = base + vp.off_a;
   void* O = base + vp.off_o;
   void* H = base + vp.off_h;
+  int2* tokw = reinterpret_cast<int2*>(base + vp.off_tokw);
+  int32_t* outrow = reinterpret_cast<int32_t*>(base + vp.off_outrow);
+  PlanEntry* planw = reinterpret_cast<PlanEntry*>(base + vp.off_planw);
   QkvOut qo{base + vp.off_q, base + vp.off_k, base + vp.off_vt, tok, rope, (int)vp.P, c->dim};
+  QkvOut qow{base + vp.off_q, base + vp.off_k, base + vp.off_vt, tokw, rope, (int)vp.Pw, c->dim};
 
   for (int c0 = 0; c0 < n_img; c0 += kDescChunk) {
     DescChunk dc{};
@@ -422,7 +472,20 @@ qv_status qv_vision_forward(const qv_vision_cfg* c, const qv_vision_w* w, const 
     QV_HIP(launch_setup_plan(vp.plan.data() + c0, dc.count, c0, plan, s));
   }
   QV_HIP(launch_rope_table(rope, vp.max_pos, c->rope_theta, s));
-  if (vp.padded) QV_HIP(launch_zero(base + vp.off_q, vp.off_vt_end - vp.off_q, s));
+  if (vp.padded || vp.window) QV_HIP(launch_zero(base + vp.off_q, vp.off_vt_end - vp.off_q, s));
+  if (vp.window) {
+    for (int c0 = 0; c0 < n_img; c0 += kDescChunk) {
+      DescChunk dc{};
+      dc.count = std::min(kDescChunk, n_img - c0);
+      dc.first = c0;
+      for (int i = 0; i < dc.count; ++i) dc.d[i] = vp.desc[c0 + i];
+      QV_HIP(launch_setup_windows(dc, vp.window, tokw, outrow, s));
+    }
+    for (int64_t c0 = 0; c0 < vp.n_win; c0 += kPlanChunk) {
+      const int cnt = (int)std::min<int64_t>(kPlanChunk, vp.n_win - c0);
+      QV_HIP(launch_setup_plan(vp.plan_w.data() + c0, cnt, (int)c0, planw, s));
+    }
+  }
 
   const int M = (int)vp.N, D = c->dim, F = c->mlp;
   const bool bf = c->dtype == QV_BF16;
@@ -433,7 +496,10 @@ qv_status qv_vision_forward(const qv_vision_cfg* c, const qv_vision_w* w, const 
     QV_LAUNCH(QV_KC_PATCH_EMBED, s, gemm_f32_store(reinterpret_cast<const float*>(patches), c->ld, reinterpret_cast<const float*>(w->patch_w),
                           c->patch_dim, M, D, c->patch_dim, reinterpret_cast<const float*>(w->patch_b), hidden, D, s));
 
-  AttnArgs aa{qo.q, qo.k, qo.vt, O, D, cu_seqlens, plan, n_img, (int)vp.P, c->heads, vp.total_qtiles, vp.attn_rows};
+  AttnArgs aa{qo.q, qo.k, qo.vt, O, D, cu_seqlens, plan, n_img, nullptr, (int)vp.P, c->heads, vp.total_qtiles,
+              vp.attn_rows};
+  AttnArgs aw{qo.q, qo.k, qo.vt, O, D, cu_seqlens, planw, (int)vp.n_win, outrow, (int)vp.Pw, c->heads,
+              vp.total_qtiles_w, bf ? 64 : kAttnBQ_f32};
   // bf16 path: at the start of block l the side stream warms block l's
   // proj / fc1 / fc2 weights and block l + 1's qkv weights, in the order the
   // GEMMs need them; the caller's stream waits for the side stream at the end.
@@ -451,17 +517,21 @@ qv_status qv_vision_forward(const qv_vision_cfg* c, const qv_vision_w* w, const 
       QV_HIP(launch_warm(b.fc2_w, (size_t)D * F * wb, wc->side));
       if (l + 1 < c->depth) QV_HIP(launch_warm(w->blocks[l + 1].qkv_w, (size_t)3 * D * D * wb, wc->side));
     }
+    // windowed block: q/k/v scattered into the window layout, attention per window
+    const bool win = vp.window && !(l < 64 && ((c->full_blocks >> l) & 1u));
+    const QkvOut& qb = win ? qow : qo;
+    const AttnArgs& ab = win ? aw : aa;
     QV_LAUNCH(QV_KC_LAYERNORM, s, launch_layernorm(hidden, (const float*)b.ln1_w, (const float*)b.ln1_b, A, bf, M, D, c->ln_eps, s));
     if (bf) {
-      QV_LAUNCH(QV_KC_QKV, s, gemm_bf16_qkv(A, D, b.qkv_w, D, M, D, (const float*)b.qkv_b, qo, s));
-      QV_LAUNCH(QV_KC_ATTENTION, s, attention_bf16(aa, s));
+      QV_LAUNCH(QV_KC_QKV, s, gemm_bf16_qkv(A, D, b.qkv_w, D, M, D, (const float*)b.qkv_b, qb, s));
+      QV_LAUNCH(QV_KC_ATTENTION, s, attention_bf16(ab, s));
       QV_LAUNCH(QV_KC_PROJ, s, gemm_bf16_resid_f32(O, D, b.proj_w, D, M, D, D, (const float*)b.proj_b, hidden, D, s));
     } else {
       float* qkv = reinterpret_cast<float*>(base + vp.off_qkv);
       QV_LAUNCH(QV_KC_QKV, s, gemm_f32_store((const float*)A, D, (const float*)b.qkv_w, D, M, 3 * D, D, (const float*)b.qkv_b, qkv,
                             3 * D, s));
-      QV_LAUNCH(QV_KC_QKV, s, rope_scatter_f32(qkv, M, nullptr, qo, s));
-      QV_LAUNCH(QV_KC_ATTENTION, s, attention_f32(aa, s));
+      QV_LAUNCH(QV_KC_QKV, s, rope_scatter_f32(qkv, M, nullptr, qb, s));
+      QV_LAUNCH(QV_KC_ATTENTION, s, attention_f32(ab, s));
       QV_LAUNCH(QV_KC_PROJ, s, gemm_f32_resid((const float*)O, D, (const float*)b.proj_w, D, M, D, D, (const float*)b.proj_b, hidden,
                             D, s));
     }

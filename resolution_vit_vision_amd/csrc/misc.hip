@@ -96,10 +96,49 @@ hipError_t launch_setup_tokens(const DescChunk& c, int2* tokinfo, hipStream_t s)
   return hipGetLastError();
 }
 
+// Windowed attention layout.  Windows tile each frame's patch grid from the
+// top-left corner in steps of `window` patches (edge windows are truncated);
+// window (t, wy, wx) of image i is global window wbase + (t * nwy + wy) * nwx
+// + wx and occupies padded rows [kSeqAlign * global window, + its size).
+// Inside a window the tokens keep their packed (merge-group) order: group
+// (bh', bw') of the window's ww/2 groups per row, member q = 2 dy + dx.
+__global__ __launch_bounds__(256) void k_setup_windows(DescChunk c, int window, int2* __restrict__ tokinfo_w,
+                                                       int32_t* __restrict__ out_row) {
+  const int img = blockIdx.y;
+  if (img >= c.count) return;
+  const ImgDesc d = c.d[img];
+  const int s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (s >= d.n) return;
+  const int hw = d.gh * d.gw;
+  const int t = s / hw, rem = s % hw;
+  const int blk = rem >> 2, q = rem & 3;
+  const int half_w = d.gw >> 1;
+  const int h = 2 * (blk / half_w) + (q >> 1);
+  const int w = 2 * (blk % half_w) + (q & 1);
+  const int wy = h / window, wx = w / window;
+  const int ww = min(window, d.gw - wx * window);
+  const int hl = h - wy * window, wl = w - wx * window;
+  const int local = ((hl >> 1) * (ww >> 1) + (wl >> 1)) * 4 + q;
+  const int gwin = d.wbase + (t * d.nwy + wy) * d.nwx + wx;
+  const int prow = gwin * kSeqAlign + local;
+  tokinfo_w[d.row0 + s] = make_int2(h | (w << 16), prow);
+  out_row[prow] = d.row0 + s;
+}
+
+hipError_t launch_setup_windows(const DescChunk& c, int window, int2* tokinfo_w, int32_t* out_row,
+                                hipStream_t s) {
+  int nmax = 0;
+  for (int i = 0; i < c.count; ++i) nmax = c.d[i].n > nmax ? c.d[i].n : nmax;
+  if (nmax == 0) return hipSuccess;
+  dim3 grid((unsigned)((nmax + 255) / 256), (unsigned)c.count);
+  hipLaunchKernelGGL(k_setup_windows, grid, dim3(256), 0, s, c, window, tokinfo_w, out_row);
+  return hipGetLastError();
+}
+
 struct PlanChunk {
   int32_t count;
   int32_t first;
-  PlanEntry e[kDescChunk];
+  PlanEntry e[kPlanChunk];
 };
 
 __global__ void k_setup_plan(PlanChunk c, PlanEntry* __restrict__ plan) {
@@ -113,7 +152,7 @@ hipError_t launch_setup_plan(const PlanEntry* host_plan_chunk, int count, int fi
   c.count = count;
   c.first = first;
   for (int i = 0; i < count; ++i) c.e[i] = host_plan_chunk[i];
-  hipLaunchKernelGGL(k_setup_plan, dim3(1), dim3(64), 0, s, c, plan);
+  hipLaunchKernelGGL(k_setup_plan, dim3(1), dim3(kPlanChunk), 0, s, c, plan);
   return hipGetLastError();
 }
 

@@ -17,21 +17,27 @@ struct ImgDesc {
   int32_t n;      // patches T*gh*gw
   int32_t t, gh, gw;
   int32_t prow0;  // first row in the padded attention layout
+  int32_t wbase;  // windowed attention: global index of the image's first window
+  int32_t nwy, nwx;  // windows per frame along h and w
 };
 
 constexpr int kDescChunk = 32;
+constexpr int kPlanChunk = 128;  // plan entries per setup launch (2 KB of kernel arguments)
 struct DescChunk {
   int32_t count;
   int32_t first;  // index of d[0] in the full list
   ImgDesc d[kDescChunk];
 };
 
-// One entry of the attention work plan, images sorted by length, longest first.
+// One entry of the attention work plan, segments sorted by length, longest
+// first.  A segment is an image (rows cu_seqlens[seg] .. cu_seqlens[seg+1])
+// or, for windowed blocks, one window (length in `n`, output rows through
+// the out_row map).
 struct PlanEntry {
-  int32_t img;        // image index (into cu_seqlens)
+  int32_t seg;        // image index (into cu_seqlens) or window index
   int32_t prow0;      // padded row start
-  int32_t qtile0;     // first global q-tile of this image
-  int32_t reserved;
+  int32_t qtile0;     // first global q-tile of this segment
+  int32_t n;          // window length (window plans only)
 };
 
 // Patchify: one image per chunk entry.
@@ -53,6 +59,11 @@ hipError_t launch_patchify(const float* pixels, const PatchChunk& c, int patch, 
                            bool bf16, int ld, int patch_dim, int64_t rows_in_chunk_max, hipStream_t s);
 
 hipError_t launch_setup_tokens(const DescChunk& c, int2* tokinfo, hipStream_t s);
+// windowed attention: tokinfo_w[row] = {h | w << 16, padded row in the window
+// layout (window index * kSeqAlign + place in the window)} and
+// out_row[padded row] = packed row, for windows of `window` patches
+hipError_t launch_setup_windows(const DescChunk& c, int window, int2* tokinfo_w, int32_t* out_row,
+                                hipStream_t s);
 hipError_t launch_setup_plan(const PlanEntry* host_plan_chunk, int count, int first, PlanEntry* plan,
                              hipStream_t s);
 hipError_t launch_rope_table(float2* tab, int positions, float theta, hipStream_t s);
@@ -110,7 +121,8 @@ struct AttnArgs {
   int ldo;
   const int32_t* cu_seqlens;
   const PlanEntry* plan;
-  int n_img;
+  int n_img;                 // plan entries (images or windows)
+  const int32_t* out_row;    // null: segments are images; else window plan, packed row of each padded row
   int P;
   int heads;
   int total_qtiles;

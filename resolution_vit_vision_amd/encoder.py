@@ -97,10 +97,17 @@ class VisionConfig:
     dtype: str = "bf16"
     ln_eps: float = 1e-6
     rope_theta: float = 1e4
+    window: int = 0                 # window side in patches (0: full attention in every block)
+    full_blocks: Tuple[int, ...] = ()  # blocks that keep full attention when window > 0
 
     def c(self) -> _abi.VisionCfg:
+        mask = 0
+        for b in self.full_blocks:
+            if not 0 <= b < 64:
+                raise ValueError(f"full-attention block {b} outside 0..63")
+            mask |= 1 << b
         return _abi.VisionCfg(self.depth, self.dim, self.heads, self.mlp, self.patch_dim, self.ld, self.merge,
-                              DTYPES[self.dtype], self.ln_eps, self.rope_theta)
+                              DTYPES[self.dtype], self.ln_eps, self.rope_theta, self.window, 0, mask)
 
 
 @dataclass
@@ -207,7 +214,7 @@ class Encoder:
 
     def __init__(self, params: Dict[str, np.ndarray], images: Sequence[np.ndarray], depth: int, out_dim: int,
                  dtype: str = "bf16", dim: int = 1280, heads: int = 16, mlp: int = 5120, ln_eps: float = 1e-6,
-                 rope_theta: float = 1e4, device="cuda", grids=None, **grid_kw):
+                 rope_theta: float = 1e4, window: int = 0, full_blocks=(), device="cuda", grids=None, **grid_kw):
         self.dtype = dtype
         self.grid_kw = grid_kw
         if grids is None:
@@ -224,7 +231,8 @@ class Encoder:
         self.n = int(cu[-1])
         pd = images[0].shape[1] * 2 * 14 * 14
         self.vcfg = VisionConfig(depth=depth, dim=dim, heads=heads, mlp=mlp, patch_dim=pd, ld=pd, dtype=dtype,
-                                 ln_eps=ln_eps, rope_theta=rope_theta)
+                                 ln_eps=ln_eps, rope_theta=rope_theta, window=window,
+                                 full_blocks=tuple(full_blocks))
         self.mcfg = MergerConfig(dim=dim, out_dim=out_dim, dtype=dtype, ln_eps=ln_eps)
         self.vw = VisionWeights(params, depth, dtype, device)
         self.mw = MergerWeights(params, dtype, device)

@@ -54,6 +54,8 @@ class Workload:
     rope_theta: float = 1e4
     seed: int = 0
     tol: float = 2e-2                          # rel-L2 bar for this dtype
+    window: int = 0                            # attention window side in patches (0: none)
+    full_blocks: Tuple[int, ...] = ()          # blocks with full attention when windowed
     description: str = ""
 
     @property
@@ -89,11 +91,18 @@ def _workloads() -> Dict[str, Workload]:
     maxres = Workload(
         name="maxres_3584", images=((3584, 3584, 1),), depth=32, out_dim=3584,
         description="one 3584x3584 image, 256x256 grid, 32 blocks, merger to 3584, bf16")
-    return {w.name: w for w in (toy, w448, w672x4, mixed, maxres)}
+    maxres_win = Workload(
+        name="qwen25vl_7b_3584_window", images=((3584, 3584, 1),), depth=32, out_dim=3584, window=8,
+        full_blocks=(7, 15, 23, 31),
+        description="one 3584x3584 image, 256x256 grid, 32 blocks attending in 8x8-patch windows "
+                    "except blocks 7/15/23/31, merger to 3584, bf16")
+    return {w.name: w for w in (toy, w448, w672x4, mixed, maxres, maxres_win)}
 
 
 WORKLOADS: Dict[str, Workload] = _workloads()
-TOY, W448, W672X4, MIXED16, MAXRES = (WORKLOADS[k] for k in list(WORKLOADS))
+TOY, W448, W672X4, MIXED16, MAXRES, MAXRES_WIN = (
+    WORKLOADS[k] for k in ("toy_112_fp32", "qwen2vl_2b_448", "qwen2vl_2b_672x4_varlen", "mixed16_varlen_7b_merger",
+                           "maxres_3584", "qwen25vl_7b_3584_window"))
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:

@@ -206,7 +206,7 @@ def _sampled_rows(cu, rng, per_image=4):
     return np.unique(np.asarray(rows))
 
 
-FULL = ["qwen2vl_2b_672x4_varlen", "mixed16_varlen_7b_merger", "maxres_3584"]
+FULL = ["qwen2vl_2b_672x4_varlen", "mixed16_varlen_7b_merger", "maxres_3584", "qwen25vl_7b_3584_window"]
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -220,9 +220,11 @@ def test_full_size_sampled(name):
     params = synth.params(wl)
     imgs = synth.pixels(wl)
     grids = [O.grid_thw(h, w, f)[2] for h, w, f in wl.images]
-    enc = qv.Encoder(params, imgs, depth=wl.depth, out_dim=wl.out_dim, dtype=wl.dtype)
+    enc = qv.Encoder(params, imgs, depth=wl.depth, out_dim=wl.out_dim, dtype=wl.dtype, window=wl.window,
+                     full_blocks=wl.full_blocks)
     assert enc.grids == [tuple(g) for g in grids]
     cu, pos, _ = O.seq_meta(grids)
+    windows = O.window_groups(grids, wl.window) if wl.window else None
     assert np.array_equal(enc.cu_host, cu)
     rng = np.random.default_rng(7)
     enc.run()
@@ -235,14 +237,15 @@ def test_full_size_sampled(name):
     hid_full = _host(enc.hidden)
     angles = O.rope_angles(pos)
     rows = _sampled_rows(cu, rng)
-    for l in (0, wl.depth - 1):
+    for l in ((0, wl.depth - 1) if not wl.window else (0, wl.full_blocks[0], wl.depth - 1)):
         z_in = _host(qv.vision_forward(enc.vcfg.__class__(**{**enc.vcfg.__dict__, "depth": l}), enc.vw,
                                        enc.patches, enc.grids, enc.cu, ws=enc.ws)).astype(np.float64)
         z_out = _host(qv.vision_forward(enc.vcfg.__class__(**{**enc.vcfg.__dict__, "depth": l + 1}), enc.vw,
                                         enc.patches, enc.grids, enc.cu, ws=enc.ws))
         torch.cuda.synchronize()
-        _say(f"{name}: block {l} teacher-forced on {len(rows)} rows")
-        ref = O.vision_block_rows(z_in, O.block_params(params, l), cu, angles, rows)
+        groups = windows if (windows is not None and l not in wl.full_blocks) else None
+        _say(f"{name}: block {l} ({'windowed' if groups else 'full'}) teacher-forced on {len(rows)} rows")
+        ref = O.vision_block_rows(z_in, O.block_params(params, l), cu, angles, rows, groups=groups)
         e = rel_l2(z_out[rows], ref)
         _say(f"  block {l} rel-L2 {e:.3e}")
         assert e <= wl.tol

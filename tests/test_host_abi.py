@@ -17,7 +17,7 @@ def test_library_exports_every_header_symbol():
     assert len(names) >= 10
     missing = [n for n in names if not hasattr(L, n)]
     assert not missing, missing
-    assert L.qv_abi_version() == 1
+    assert L.qv_abi_version() == 2
 
 
 def test_grid_params_default():
@@ -118,10 +118,19 @@ def test_vision_forward_validation():
     assert _vforward(_vcfg(dtype=7), [(1, 4, 4)]) == _abi.QV_ERR_UNSUPPORTED
     assert _vforward(_vcfg(), [(1, 4, 4)], ws_bytes=1024) == _abi.QV_ERR_WORKSPACE
     assert _vforward(_vcfg(), [(1, 4, 4)], null_block=True) == _abi.QV_ERR_NULL
+    assert _vforward(_vcfg(window=3), [(1, 4, 4)]) == _abi.QV_ERR_UNSUPPORTED   # not a multiple of merge
+    assert _vforward(_vcfg(window=12), [(1, 4, 4)]) == _abi.QV_ERR_UNSUPPORTED  # more than 100 patches
+    assert _vforward(_vcfg(window=-2), [(1, 4, 4)]) == _abi.QV_ERR_UNSUPPORTED
+    assert _vforward(_vcfg(window=8, reserved0=1), [(1, 4, 4)]) == _abi.QV_ERR_SHAPE
     n = ctypes.c_size_t()
     g = np.array([[1, 32, 32]], np.int32)
     assert L.qv_vision_workspace_size(ctypes.byref(_vcfg()), g.ctypes.data, 1, ctypes.byref(n)) == 0
     assert n.value > 1024 * 1280 * 2
+    # the window layout (one 128-row slot per window) can need more room than
+    # the image layout: 32 x 32 patches in 2 x 2 windows = 256 windows
+    nw = ctypes.c_size_t()
+    assert L.qv_vision_workspace_size(ctypes.byref(_vcfg(window=2)), g.ctypes.data, 1, ctypes.byref(nw)) == 0
+    assert nw.value > n.value
 
 
 def test_patchify_validation():

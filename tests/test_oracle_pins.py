@@ -406,6 +406,24 @@ def test_block_rows_equals_block():
     np.testing.assert_allclose(O.vision_block_rows(z, p, cu, a, rows), full[rows], rtol=1e-10, atol=1e-12)
 
 
+def test_block_rows_equals_block_windowed():
+    """Sampled rows of a windowed block (ragged edge windows) equal the whole
+    windowed block at those rows."""
+    rng = np.random.default_rng(14)
+    p = _block_params(rng)
+    grids = [(1, 6, 10), (2, 4, 2)]
+    cu, pos, _ = O.seq_meta(grids)
+    z = rng.standard_normal((cu[-1], 1280))
+    a = O.rope_angles(pos)
+    g = O.window_groups(grids, 4)
+    full = O.vision_block(z, p, cu, a, groups=g)
+    rows = np.array([0, 7, 22, 45, 59, 60, 71, 75])
+    np.testing.assert_allclose(O.vision_block_rows(z, p, cu, a, rows, groups=g), full[rows],
+                               rtol=1e-10, atol=1e-12)
+    # and they differ from the full-attention rows (the windows matter here)
+    assert not np.allclose(O.vision_block_rows(z, p, cu, a, rows), full[rows])
+
+
 # ---------------------------------------------------------------- merger
 def test_merger_identity_special_case_and_shapes():
     """fc1 = I, b1 = 0, fc2 = I[:out], b2 = 0 leaves GELU(LN(z) grouped) — pins
