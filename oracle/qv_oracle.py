@@ -18,6 +18,12 @@ title and section):
               rewrite / No GATHER_ND bullets]
   patchify    2x14x14x3 temporal patches, a still frame duplicated
               [LiteRT-LM card, Conversion notes: Conv3d -> Conv2d fold]
+  normalize   optional per-channel CLIP normalisation of the pixels
+              [ZeroModels docs, Qwen2VLImageProcessor table: image_mean,
+              image_std]
+  fold        still images: the duplicated frame folded into a Conv2d
+              weight summed over the temporal taps, K = C*14*14
+              [LiteRT-LM card, Conversion notes: Conv3d -> Conv2d fold]
   patch_embed Conv3d with kernel = stride = (2,14,14) as a matrix product
   rope        2-D rotary positions over the (h, w) patch grid
               [Neurarch Qwen2-VL card, Structure table row "2D RoPE";
@@ -60,6 +66,8 @@ MERGE = 2
 TEMPORAL = 2
 MIN_PIXELS = 3136
 MAX_PIXELS = 12845056
+CLIP_MEAN = (0.48145466, 0.4578275, 0.40821073)
+CLIP_STD = (0.26862954, 0.26130258, 0.27577711)
 
 
 # ---------------------------------------------------------------- grid (integer)
@@ -171,6 +179,63 @@ def patchify(images: Sequence[np.ndarray], grids: Sequence[Tuple[int, int, int]]
         rows.append(r[perm[start:start + n]])
         start += n
     return np.concatenate(rows, axis=0)
+
+
+def normalize(frames: np.ndarray, mean: Sequence[float] = CLIP_MEAN,
+              std: Sequence[float] = CLIP_STD) -> np.ndarray:
+    """Per-channel normalisation (x - mean_c) / std_c of [F][C][H][W] pixels,
+    in float32 arithmetic (one subtraction, one division per value), with the
+    processor's CLIP mean and std by default [ZeroModels docs,
+    Qwen2VLImageProcessor table].  Reading: the pixels are already rescaled
+    to [0, 1]; the rescale itself is the caller's."""
+    x = np.asarray(frames, dtype=np.float32)
+    c = x.shape[1]
+    m = np.asarray(mean, dtype=np.float32)[:c].reshape(1, c, 1, 1)
+    sd = np.asarray(std, dtype=np.float32)[:c].reshape(1, c, 1, 1)
+    return (x - m) / sd
+
+
+def patchify_folded(images: Sequence[np.ndarray], grids: Sequence[Tuple[int, int, int]],
+                    merge: int = MERGE, patch: int = PATCH, width: int | None = None) -> np.ndarray:
+    """Patch matrix of still images for the folded (Conv2d) patch-embed:
+    row = the [C][14][14] pixels of the patch in the single frame, in the
+    same merge-group order as ``patchify``; columns past C*14*14 up to
+    ``width`` are zero.  A still image is duplicated into both temporal
+    slots of the Conv3d, so the product with the temporally summed weight
+    (``fold_patch_weight``) equals the Conv3d result [LiteRT-LM card,
+    Conversion notes: Conv3d -> Conv2d fold].  Images with more than one
+    frame are rejected: their temporal slots differ."""
+    _, _, perm = seq_meta(grids, merge)
+    rows = []
+    start = 0
+    for img, (t, gh, gw) in zip(images, grids):
+        f, c, hh, ww = img.shape
+        if f != 1 or t != 1:
+            raise ValueError("the Conv2d fold applies to single-frame images only")
+        if hh != gh * patch or ww != gw * patch:
+            raise ValueError("image sides must equal grid * patch (no resampling)")
+        x = img[0].reshape(c, gh, patch, gw, patch).transpose(1, 3, 0, 2, 4).reshape(gh * gw, c * patch * patch)
+        rows.append(x[perm[start:start + gh * gw]])
+        start += gh * gw
+    out = np.concatenate(rows, axis=0)
+    if width is not None and width > out.shape[1]:
+        out = np.concatenate([out, np.zeros((out.shape[0], width - out.shape[1]), out.dtype)], axis=1)
+    return out
+
+
+def fold_patch_weight(w: np.ndarray, width: int | None = None) -> np.ndarray:
+    """Conv3d weight [out][C][T][p][p] -> Conv2d weight [out][C*p*p], summed
+    over the T temporal taps in tap order (in the weight's own precision),
+    zero-padded to ``width`` columns [LiteRT-LM card, Conversion notes:
+    Conv3d -> Conv2d fold]."""
+    o, c, t, p, q = w.shape
+    acc = w[:, :, 0]
+    for tau in range(1, t):
+        acc = acc + w[:, :, tau]
+    out = acc.reshape(o, c * p * q)
+    if width is not None and width > out.shape[1]:
+        out = np.concatenate([out, np.zeros((o, width - out.shape[1]), out.dtype)], axis=1)
+    return out
 
 
 # -------------------------------------------------------------- elementwise ops
@@ -467,9 +532,12 @@ def patch_merge(z: np.ndarray, params: Dict[str, np.ndarray], merge: int = MERGE
 def encode(images: Sequence[np.ndarray], params: Dict[str, np.ndarray], depth: int,
            heads: int = 16, eps: float = 1e-6, theta: float = 1e4, dtype=np.float64,
            min_pixels: int = MIN_PIXELS, max_pixels: int = MAX_PIXELS, window: int = 0,
-           full_blocks: Sequence[int] = ()):
+           full_blocks: Sequence[int] = (), normalize_pixels: bool = False):
     """Whole path for images whose sides already sit on the grid:
-    grid -> patchify -> tower -> merger.  Returns (grids, hidden, merged)."""
+    grid -> (normalize) -> patchify -> tower -> merger.  Returns (grids,
+    hidden, merged).  Always the Conv3d definition (no fold)."""
+    if normalize_pixels:
+        images = [normalize(im) for im in images]
     grids = []
     for img in images:
         f, _, h, w = img.shape

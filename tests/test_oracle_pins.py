@@ -615,3 +615,61 @@ def test_windowed_block_isolates_windows():
     out = O.vision_block(z2, p, cu, angles, heads=4, groups=groups)
     changed = np.nonzero(np.any(np.abs(out - base) > 0, axis=1))[0]
     np.testing.assert_array_equal(np.sort(changed), np.sort(groups[1]))
+
+
+# ------------------------------------------------ Conv2d fold, CLIP normalisation
+def test_fold_identity_equals_conv3d():
+    """Still images: folded patches x temporally summed weight == the Conv3d
+    product over the duplicated frame (the LiteRT-LM fold), in float64."""
+    rng = np.random.default_rng(21)
+    sides = [(56, 84), (28 * 3, 28 * 2)]
+    imgs = [rng.uniform(-1, 1, (1, 3, h, w)) for h, w in sides]
+    grids = [O.grid_thw(h, w, 1)[2] for h, w in sides]
+    w3 = rng.standard_normal((64, 3, 2, 14, 14))
+    ref = O.patch_embed(O.patchify(imgs, grids), w3)
+    xf = O.patchify_folded(imgs, grids, width=592)
+    wf = O.fold_patch_weight(w3, width=592)
+    assert xf.shape == (ref.shape[0], 592) and wf.shape == (64, 592)
+    np.testing.assert_allclose(xf @ wf.T, ref, rtol=1e-12, atol=1e-12)
+    # a weight whose two taps differ shows the sum is over the temporal axis
+    # (not over channels or rows): tap 1 = 0 leaves half the Conv3d product
+    w_half = w3.copy()
+    w_half[:, :, 1] = 0
+    np.testing.assert_allclose(O.patchify_folded(imgs, grids) @ O.fold_patch_weight(w_half).T,
+                               O.patch_embed(O.patchify(imgs, grids), w_half), rtol=1e-12, atol=1e-12)
+
+
+def test_folded_rows_are_the_first_temporal_slice_and_pads_zero():
+    rng = np.random.default_rng(22)
+    imgs = [rng.uniform(0, 1, (1, 3, 56, 112)).astype(np.float32)]
+    grids = [(1, 4, 8)]
+    full = O.patchify(imgs, grids).reshape(32, 3, 2, 14, 14)
+    xf = O.patchify_folded(imgs, grids, width=600)
+    assert np.array_equal(xf[:, :588].reshape(32, 3, 14, 14), full[:, :, 0])
+    assert np.array_equal(full[:, :, 0], full[:, :, 1])  # the still frame is duplicated
+    assert (xf[:, 588:] == 0).all()
+    # hand-listed element: merge-group slot 5 is (block row 0, block col 1,
+    # dy 0, dx 1) -> patch (h 0, w 3); element (c 2, r 3, q 4)
+    assert xf[5, 2 * 196 + 3 * 14 + 4] == imgs[0][0, 2, 3, 3 * 14 + 4]
+
+
+def test_fold_rejects_multi_frame_images():
+    img = np.zeros((2, 3, 28, 28), np.float32)
+    with pytest.raises(ValueError):
+        O.patchify_folded([img], [(1, 2, 2)])
+
+
+def test_normalize_closed_forms():
+    m = np.array(O.CLIP_MEAN, np.float32)
+    s = np.array(O.CLIP_STD, np.float32)
+    x = np.stack([np.full((2, 2), m[c]) for c in range(3)])[None].astype(np.float32)
+    assert (O.normalize(x) == 0).all()                      # the mean maps to 0
+    y = O.normalize(x + s.reshape(1, 3, 1, 1))              # one std above -> ~1
+    np.testing.assert_allclose(y, 1.0, rtol=0, atol=2e-7)
+    # channel order: a grey pixel of 0.5 lands at (0.5 - mean_c) / std_c per channel
+    g = O.normalize(np.full((1, 3, 1, 1), 0.5, np.float32))[0, :, 0, 0]
+    np.testing.assert_allclose(g, [(0.5 - 0.48145466) / 0.26862954, (0.5 - 0.4578275) / 0.26130258,
+                                   (0.5 - 0.40821073) / 0.27577711], rtol=1e-6)
+    # the CLIP constants of the processor table
+    assert O.CLIP_MEAN == (0.48145466, 0.4578275, 0.40821073)
+    assert O.CLIP_STD == (0.26862954, 0.26130258, 0.27577711)
