@@ -30,7 +30,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
-def workload_flops(wl, grids):
+def workload_flops(wl, grids, fold=False):
     """Algorithmic FLOPs of one step: true K (1176), block-diagonal attention
     (sum n_i^2 over images, or over windows in the windowed blocks), matrix
     products only.  "attention" is the average over the step's blocks."""
@@ -49,7 +49,7 @@ def workload_flops(wl, grids):
         nfull = sum(1 for b in wl.full_blocks if b < wl.depth)
         att = (nfull * att_full + (wl.depth - nfull) * 4 * d * sq) / wl.depth
     per = {
-        "patch_embed": 2 * n * pd * d,
+        "patch_embed": 2 * n * (wl.in_channels * wl.patch * wl.patch if fold else pd) * d,
         "qkv": 2 * n * d * 3 * d,
         "attention": att,
         "proj": 2 * n * d * d,
@@ -127,6 +127,8 @@ def main():
     ap.add_argument("--workload", default="qwen2vl_2b_448")
     ap.add_argument("--roofline-kernel", default=None, help="kernel class for the roofline (default: slowest)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fold", action="store_true",
+                    help="keep the Conv3d patch-embed (K = 1176) for still images")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
 
@@ -151,12 +153,13 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     params = synth.params(wl)
     imgs = synth.pixels(wl)
+    fold = not args.no_fold and all(f == 1 for _, _, f in wl.images)
     enc = qv.Encoder(params, imgs, depth=wl.depth, out_dim=wl.out_dim, dtype=wl.dtype, window=wl.window,
-                     full_blocks=wl.full_blocks)
+                     full_blocks=wl.full_blocks, fold=fold)
     grids = enc.grids
     n = enc.n
     m = n // 4
-    flops, per = workload_flops(wl, grids)
+    flops, per = workload_flops(wl, grids, fold)
 
     for _ in range(max(args.warmup, 1)):
         enc.run()
@@ -229,7 +232,8 @@ def main():
         "config": {"workload": wl.name, "images": [f"{h}x{w}" for h, w, _ in wl.images][:4]
                    + (["..."] if len(wl.images) > 4 else []),
                    "n_images": len(wl.images), "patches": n, "merged_tokens": m, "depth": wl.depth,
-                   "out_dim": wl.out_dim, "window": wl.window, "full_blocks": list(wl.full_blocks)},
+                   "out_dim": wl.out_dim, "window": wl.window, "full_blocks": list(wl.full_blocks),
+                   "patch_embed": "conv2d fold, K=592" if fold else "conv3d, K=1176"},
         "patches_per_s": n * args.steps / (ms / 1e3),
         "algorithmic_tflop_per_step": flops / 1e12,
         "achieved_tflops": flops / (ms_per_step / 1e3) / 1e12,

@@ -146,6 +146,52 @@ qv_status qv_patchify(const float *pixels, const qv_image *images, int32_t n_img
                       const int32_t *grid_thw, const qv_grid_params *p, void *patches,
                       qv_dtype out_dtype, int32_t ld, void *stream);
 
+/* Options of qv_patchify_ex.
+ * fold: still images (every image has one frame, so T == 1) only.  The
+ *   duplicated frame is folded into the weight (LiteRT-LM card, Conversion
+ *   notes: Conv3d -> Conv2d fold): row element (c*patch + r)*patch + q is
+ *   pixel frame[0][c][patch*h + r][patch*w + q], width channels*patch^2
+ *   (588), then zeros up to the next multiple of 8 (592).  Pair it with a
+ *   weight from qv_fold_patch_weight and qv_vision_cfg.patch_dim = 592.
+ * normalize: each pixel becomes (x - mean[c]) / std[c] in float32 (one
+ *   subtraction, one correctly rounded division) before the cast (ZeroModels
+ *   docs, Qwen2VLImageProcessor table: image_mean, image_std; the CLIP values
+ *   are QV_CLIP_MEAN / QV_CLIP_STD).  At most 4 channels; std > 0. */
+typedef struct qv_patch_opts {
+  int32_t fold;       /* 0 or 1 */
+  int32_t normalize;  /* 0 or 1 */
+  float mean[4];
+  float std[4];
+} qv_patch_opts;
+
+#define QV_CLIP_MEAN {0.48145466f, 0.4578275f, 0.40821073f, 0.0f}
+#define QV_CLIP_STD {0.26862954f, 0.26130258f, 0.27577711f, 1.0f}
+
+/* qv_patchify with options (opts NULL = qv_patchify).  Same arguments,
+ * layout and errors as qv_patchify; with fold, ld >= round_up(channels *
+ * patch^2, 8) and the pad columns up to that width are written as zeros.
+ * Extra errors: QV_ERR_SHAPE for fold with an image of more than one frame;
+ * QV_ERR_UNSUPPORTED for normalize with more than 4 channels or a std <= 0
+ * (or NaN), or flags other than 0/1. */
+qv_status qv_patchify_ex(const float *pixels, const qv_image *images, int32_t n_img,
+                         const int32_t *grid_thw, const qv_grid_params *p,
+                         const qv_patch_opts *opts, void *patches, qv_dtype out_dtype,
+                         int32_t ld, void *stream);
+
+/* Fold a Conv3d patch-embed weight into the Conv2d weight of still images
+ * (LiteRT-LM card, Conversion notes: Conv3d -> Conv2d fold).
+ * w: device [dim][ld_in] in dtype, row = [channels][temporal][patch][patch];
+ * out: device [dim][ld_out] in dtype, row element (c*patch + r)*patch + q =
+ * sum over tau = 0..temporal-1 (in that order, float32) of
+ * w[(c*temporal + tau)*patch + r)*patch + q], rounded to dtype (bf16: to
+ * nearest even); columns channels*patch^2 .. ld_out-1 are zero.
+ * ld_in >= channels*temporal*patch^2; ld_out >= channels*patch^2.
+ * Errors: QV_ERR_NULL, QV_ERR_SHAPE (sizes), QV_ERR_UNSUPPORTED (dtype),
+ * QV_ERR_HIP.  out must not overlap w. */
+qv_status qv_fold_patch_weight(const void *w, int32_t dim, int32_t channels, int32_t patch,
+                               int32_t temporal, int32_t ld_in, void *out, int32_t ld_out,
+                               qv_dtype dtype, void *stream);
+
 /* ---------------------------------------------------------- vision tower */
 
 /* Device pointers of one block.  Matrices in the tower dtype, vectors f32.

@@ -37,6 +37,14 @@ class Image(Structure):
                 ("width", c_int32), ("reserved", c_int32)]
 
 
+class PatchOpts(Structure):
+    _fields_ = [("fold", c_int32), ("normalize", c_int32), ("mean", c_float * 4), ("std", c_float * 4)]
+
+
+CLIP_MEAN = (0.48145466, 0.4578275, 0.40821073, 0.0)
+CLIP_STD = (0.26862954, 0.26130258, 0.27577711, 1.0)
+
+
 BLOCK_FIELDS = ("ln1_w", "ln1_b", "qkv_w", "qkv_b", "proj_w", "proj_b",
                 "ln2_w", "ln2_b", "fc1_w", "fc1_b", "fc2_w", "fc2_b")
 
@@ -103,6 +111,12 @@ def lib() -> ctypes.CDLL:
     L.qv_patchify.restype = c_int32
     L.qv_patchify.argtypes = [c_void_p, POINTER(Image), c_int32, c_void_p, POINTER(GridParams), c_void_p, c_int32,
                               c_int32, c_void_p]
+    L.qv_patchify_ex.restype = c_int32
+    L.qv_patchify_ex.argtypes = [c_void_p, POINTER(Image), c_int32, c_void_p, POINTER(GridParams),
+                                 POINTER(PatchOpts), c_void_p, c_int32, c_int32, c_void_p]
+    L.qv_fold_patch_weight.restype = c_int32
+    L.qv_fold_patch_weight.argtypes = [c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p, c_int32,
+                                       c_int32, c_void_p]
     L.qv_vision_workspace_size.restype = c_int32
     L.qv_vision_workspace_size.argtypes = [POINTER(VisionCfg), c_void_p, c_int32, POINTER(c_size_t)]
     L.qv_vision_forward.restype = c_int32

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <mutex>
 #include <string>
 #include <utility>
@@ -215,17 +216,34 @@ qv_status qv_seq_meta(const int32_t* grid_thw, int32_t n_img, int32_t merge, int
 
 qv_status qv_patchify(const float* pixels, const qv_image* images, int32_t n_img, const int32_t* grid_thw,
                       const qv_grid_params* pin, void* patches, qv_dtype out_dtype, int32_t ld, void* stream) {
+  return qv_patchify_ex(pixels, images, n_img, grid_thw, pin, nullptr, patches, out_dtype, ld, stream);
+}
+
+qv_status qv_patchify_ex(const float* pixels, const qv_image* images, int32_t n_img, const int32_t* grid_thw,
+                         const qv_grid_params* pin, const qv_patch_opts* opts, void* patches, qv_dtype out_dtype,
+                         int32_t ld, void* stream) {
   qv_grid_params p;
   if (pin) p = *pin; else qv_grid_params_default(&p);
+  qv_patch_opts o{};
+  if (opts) o = *opts;
   if (!pixels || !images || !patches) return fail(QV_ERR_NULL, "pixels, images and patches must be non-NULL");
   if (p.merge != 2) return fail(QV_ERR_UNSUPPORTED, "only merge 2 is implemented");
   if (out_dtype != QV_F32 && out_dtype != QV_BF16) return fail(QV_ERR_UNSUPPORTED, "unknown dtype %d", (int)out_dtype);
+  if ((o.fold != 0 && o.fold != 1) || (o.normalize != 0 && o.normalize != 1))
+    return fail(QV_ERR_UNSUPPORTED, "fold and normalize must be 0 or 1");
   std::vector<Grid> g;
   int64_t total = 0;
   qv_status st = read_grids(grid_thw, n_img, p.merge, g, total);
   if (st != QV_OK) return st;
   const int channels = images[0].channels;
-  const int patch_dim = channels * p.temporal * p.patch * p.patch;
+  if (o.normalize) {
+    if (channels > 4) return fail(QV_ERR_UNSUPPORTED, "normalize supports at most 4 channels, got %d", channels);
+    for (int ch = 0; ch < channels; ++ch)
+      if (!(o.std[ch] > 0.f) || !std::isfinite(o.mean[ch]))
+        return fail(QV_ERR_UNSUPPORTED, "normalize: std[%d] must be > 0 and mean[%d] finite", ch, ch);
+  }
+  const int vec = channels * (o.fold ? 1 : p.temporal) * p.patch * p.patch;
+  const int patch_dim = o.fold ? (vec + 7) / 8 * 8 : vec;
   if (patch_dim % 8) return fail(QV_ERR_UNSUPPORTED, "patch vector length %d is not a multiple of 8", patch_dim);
   if (ld < patch_dim || ld % 8) return fail(QV_ERR_SHAPE, "ld %d must be >= %d and a multiple of 8", ld, patch_dim);
   std::vector<PatchImg> d(n_img);
@@ -240,8 +258,18 @@ qv_status qv_patchify(const float* pixels, const qv_image* images, int32_t n_img
                   g[i].gw);
     if (g[i].t != (im.frames + p.temporal - 1) / p.temporal)
       return fail(QV_ERR_SHAPE, "image %d: T=%d but %d frames", i, g[i].t, im.frames);
+    if (o.fold && im.frames != 1)
+      return fail(QV_ERR_SHAPE, "image %d: the Conv2d fold needs a single frame, got %d", i, im.frames);
     d[i] = PatchImg{im.offset, im.frames, im.channels, im.height, im.width, g[i].t, g[i].gh, g[i].gw, (int32_t)row};
     row += (int64_t)g[i].t * g[i].gh * g[i].gw;
+  }
+  PatchMode m{};
+  m.fold = o.fold;
+  m.normalize = o.normalize;
+  m.width = patch_dim;
+  for (int ch = 0; ch < 4; ++ch) {
+    m.mean[ch] = o.mean[ch];
+    m.stdv[ch] = o.normalize ? o.std[ch] : 1.f;
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   for (int c0 = 0; c0 < n_img; c0 += kPatchChunk) {
@@ -252,8 +280,24 @@ qv_status qv_patchify(const float* pixels, const qv_image* images, int32_t n_img
       c.d[i] = d[c0 + i];
       nmax = std::max<int64_t>(nmax, (int64_t)c.d[i].t * c.d[i].gh * c.d[i].gw);
     }
-    QV_LAUNCH(QV_KC_PATCHIFY, s, launch_patchify(pixels, c, p.patch, p.temporal, patches, out_dtype == QV_BF16, ld, patch_dim, nmax, s));
+    QV_LAUNCH(QV_KC_PATCHIFY, s, launch_patchify(pixels, c, p.patch, p.temporal, patches, out_dtype == QV_BF16, ld, m, nmax, s));
   }
+  return QV_OK;
+}
+
+qv_status qv_fold_patch_weight(const void* w, int32_t dim, int32_t channels, int32_t patch, int32_t temporal,
+                               int32_t ld_in, void* out, int32_t ld_out, qv_dtype dtype, void* stream) {
+  if (!w || !out) return fail(QV_ERR_NULL, "w and out must be non-NULL");
+  if (dtype != QV_F32 && dtype != QV_BF16) return fail(QV_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+  if (dim <= 0 || channels <= 0 || patch <= 0 || temporal <= 0)
+    return fail(QV_ERR_SHAPE, "dim, channels, patch and temporal must be positive");
+  const int64_t vec_in = (int64_t)channels * temporal * patch * patch, vec_out = (int64_t)channels * patch * patch;
+  if (ld_in < vec_in || ld_out < vec_out)
+    return fail(QV_ERR_SHAPE, "ld_in %d must be >= %lld and ld_out %d >= %lld", ld_in, (long long)vec_in, ld_out,
+                (long long)vec_out);
+  if ((int64_t)dim * std::max(ld_in, ld_out) > INT32_MAX) return fail(QV_ERR_SHAPE, "weight too large");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  QV_HIP(launch_fold_weight(w, dim, channels, patch, temporal, ld_in, out, ld_out, dtype == QV_BF16, s));
   return QV_OK;
 }
 

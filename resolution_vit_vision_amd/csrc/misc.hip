@@ -10,14 +10,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) { return __builtin_
 // ------------------------------------------------------------------ patchify
 // One thread writes 8 consecutive elements of one output row.  Rows of an
 // image follow the merge-group order: slot s -> (t, block row, block col,
-// dy, dx) with dx fastest; element e -> (channel, temporal slot, row, col).
+// dy, dx) with dx fastest; element e -> (channel, temporal slot, row, col),
+// or (channel, row, col) of the single frame when the temporal slots are
+// folded into the weight; elements past the patch vector are zero.
 __global__ __launch_bounds__(256) void k_patchify(const float* __restrict__ pixels, PatchChunk c, int patch,
                                                   int temporal, void* __restrict__ out, int bf16, int ld,
-                                                  int patch_dim) {
+                                                  PatchMode m) {
   const int img = blockIdx.y;
   if (img >= c.count) return;
   const PatchImg d = c.d[img];
-  const int chunks = patch_dim / 8;
+  const int chunks = m.width / 8;
   const int64_t n = (int64_t)d.t * d.gh * d.gw;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= n * chunks) return;
@@ -31,12 +33,18 @@ __global__ __launch_bounds__(256) void k_patchify(const float* __restrict__ pixe
   const int h = 2 * (blk / half_w) + (q >> 1);
   const int w = 2 * (blk % half_w) + (q & 1);
   const int pp = patch * patch;
+  const int slots = m.fold ? 1 : temporal;      // temporal slots in the row
+  const int vec = d.channels * slots * pp;      // patch vector length
   float v[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int e = e0 + u;
-    const int ch = e / (temporal * pp);
-    const int r1 = e % (temporal * pp);
+    if (e >= vec) {
+      v[u] = 0.f;
+      continue;
+    }
+    const int ch = e / (slots * pp);
+    const int r1 = e % (slots * pp);
     const int tau = r1 / pp;
     const int r2 = r1 % pp;
     const int i = r2 / patch, j = r2 % patch;
@@ -44,7 +52,9 @@ __global__ __launch_bounds__(256) void k_patchify(const float* __restrict__ pixe
     f = f < d.frames - 1 ? f : d.frames - 1;
     const int64_t src = d.offset + (((int64_t)f * d.channels + ch) * d.height + (int64_t)patch * h + i) * d.width +
                         (int64_t)patch * w + j;
-    v[u] = pixels[src];
+    float x = pixels[src];
+    if (m.normalize) x = (x - m.mean[ch]) / m.stdv[ch];
+    v[u] = x;
   }
   const int64_t row = d.row0 + s;
   if (bf16) {
@@ -62,11 +72,46 @@ __global__ __launch_bounds__(256) void k_patchify(const float* __restrict__ pixe
 }
 
 hipError_t launch_patchify(const float* pixels, const PatchChunk& c, int patch, int temporal, void* out, bool bf16,
-                           int ld, int patch_dim, int64_t rows_in_chunk_max, hipStream_t s) {
-  const int64_t threads = rows_in_chunk_max * (patch_dim / 8);
+                           int ld, const PatchMode& m, int64_t rows_in_chunk_max, hipStream_t s) {
+  const int64_t threads = rows_in_chunk_max * (m.width / 8);
+  if (threads == 0) return hipSuccess;
   dim3 grid((unsigned)((threads + 255) / 256), (unsigned)c.count);
-  hipLaunchKernelGGL(k_patchify, grid, dim3(256), 0, s, pixels, c, patch, temporal, out, bf16 ? 1 : 0, ld,
-                     patch_dim);
+  hipLaunchKernelGGL(k_patchify, grid, dim3(256), 0, s, pixels, c, patch, temporal, out, bf16 ? 1 : 0, ld, m);
+  return hipGetLastError();
+}
+
+// Conv3d -> Conv2d weight fold: out[o][(c*p + r)*p + q] = sum over tau of
+// w[o][((c*T + tau)*p + r)*p + q], accumulated in float32 in tau order and
+// rounded once; columns past C*p*p are zero.  One thread per output element.
+__global__ __launch_bounds__(256) void k_fold_weight(const void* __restrict__ w, int dim, int channels, int patch,
+                                                     int temporal, int ld_in, void* __restrict__ out, int ld_out,
+                                                     int bf16) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)dim * ld_out) return;
+  const int o = (int)(gid / ld_out), e = (int)(gid % ld_out);
+  const int pp = patch * patch;
+  float acc = 0.f;
+  if (e < channels * pp) {
+    const int ch = e / pp, r = e % pp;
+    for (int tau = 0; tau < temporal; ++tau) {
+      const int64_t src = (int64_t)o * ld_in + ((int64_t)ch * temporal + tau) * pp + r;
+      const float x = bf16 ? __builtin_bit_cast(float, (uint32_t)reinterpret_cast<const uint16_t*>(w)[src] << 16)
+                           : reinterpret_cast<const float*>(w)[src];
+      acc = tau == 0 ? x : acc + x;
+    }
+  }
+  if (bf16)
+    reinterpret_cast<uint16_t*>(out)[gid] = f32_to_bf16_rne(acc);
+  else
+    reinterpret_cast<float*>(out)[gid] = acc;
+}
+
+hipError_t launch_fold_weight(const void* w, int dim, int channels, int patch, int temporal, int ld_in, void* out,
+                              int ld_out, bool bf16, hipStream_t s) {
+  const int64_t total = (int64_t)dim * ld_out;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fold_weight, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, w, dim, channels, patch,
+                     temporal, ld_in, out, ld_out, bf16 ? 1 : 0);
   return hipGetLastError();
 }
 

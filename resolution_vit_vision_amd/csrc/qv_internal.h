@@ -55,8 +55,18 @@ struct PatchChunk {
 enum class Act : int { None = 0, QuickGelu = 1, GeluErf = 2 };
 
 // ---- launchers (return hipGetLastError()) ----
+// Pixel transform and row shape of the patch gather.
+struct PatchMode {
+  int32_t fold;        // 1: one temporal slot (still images), rows C*patch^2 wide
+  int32_t normalize;   // 1: (x - mean[c]) / std[c]
+  int32_t width;       // elements written per row (zero beyond the patch vector)
+  int32_t reserved;
+  float mean[4], stdv[4];
+};
+hipError_t launch_fold_weight(const void* w, int dim, int channels, int patch, int temporal, int ld_in, void* out,
+                              int ld_out, bool bf16, hipStream_t s);
 hipError_t launch_patchify(const float* pixels, const PatchChunk& c, int patch, int temporal, void* out,
-                           bool bf16, int ld, int patch_dim, int64_t rows_in_chunk_max, hipStream_t s);
+                           bool bf16, int ld, const PatchMode& m, int64_t rows_in_chunk_max, hipStream_t s);
 
 hipError_t launch_setup_tokens(const DescChunk& c, int2* tokinfo, hipStream_t s);
 // windowed attention: tokinfo_w[row] = {h | w << 16, padded row in the window

@@ -69,18 +69,51 @@ def pack_images(images: Sequence[np.ndarray]):
     return flat, descs
 
 
+def patch_opts(fold: bool = False, normalize=None) -> _abi.PatchOpts:
+    """normalize: None/False (off), True (CLIP mean/std) or a (mean, std) pair."""
+    o = _abi.PatchOpts()
+    o.fold = 1 if fold else 0
+    if normalize:
+        mean, std = (_abi.CLIP_MEAN, _abi.CLIP_STD) if normalize is True else normalize
+        o.normalize = 1
+        for i in range(4):
+            o.mean[i] = float(mean[i]) if i < len(mean) else 0.0
+            o.std[i] = float(std[i]) if i < len(std) else 1.0
+    return o
+
+
+def patch_width(channels: int, fold: bool = False, patch: int = 14, temporal: int = 2) -> int:
+    """Row width of the patch matrix: C*T*p*p, or C*p*p rounded up to 8 with the fold."""
+    return (channels * patch * patch + 7) // 8 * 8 if fold else channels * temporal * patch * patch
+
+
 def patchify(pixels: torch.Tensor, descs, grids, dtype: str = "bf16", ld: int | None = None,
-             out: torch.Tensor | None = None, stream=None, **grid_kw) -> torch.Tensor:
+             out: torch.Tensor | None = None, stream=None, fold: bool = False, normalize=None,
+             **grid_kw) -> torch.Tensor:
     p = grid_params(**grid_kw)
     g = _grid_array(grids)
     arr = (_abi.Image * len(descs))(*[_abi.Image(o, f, c, h, w, 0) for (o, f, c, h, w) in descs])
     n = int((g[:, 0].astype(np.int64) * g[:, 1] * g[:, 2]).sum())
-    pd = descs[0][2] * p.temporal * p.patch * p.patch
+    pd = patch_width(descs[0][2], fold, p.patch, p.temporal)
     ld = pd if ld is None else ld
     if out is None:
         out = torch.empty((n, ld), dtype=TORCH_DTYPES[dtype], device=pixels.device)
-    check(lib().qv_patchify(_ptr(pixels), arr, len(descs), g.ctypes.data, ctypes.byref(p), _ptr(out),
-                            DTYPES[dtype], ld, _stream(stream)))
+    opts = patch_opts(fold, normalize)
+    check(lib().qv_patchify_ex(_ptr(pixels), arr, len(descs), g.ctypes.data, ctypes.byref(p), ctypes.byref(opts),
+                               _ptr(out), DTYPES[dtype], ld, _stream(stream)))
+    return out
+
+
+def fold_patch_weight(w: torch.Tensor, channels: int = 3, patch: int = 14, temporal: int = 2,
+                      ld_out: int | None = None, stream=None) -> torch.Tensor:
+    """Conv3d patch-embed weight [dim][C*T*p*p] (device, bf16 or f32) -> the
+    Conv2d weight [dim][ld_out] of still images (temporal taps summed)."""
+    dim = w.shape[0]
+    ld_out = patch_width(channels, True, patch, temporal) if ld_out is None else ld_out
+    out = torch.empty((dim, ld_out), dtype=w.dtype, device=w.device)
+    dt = "bf16" if w.dtype == torch.bfloat16 else "f32"
+    check(lib().qv_fold_patch_weight(_ptr(w), dim, channels, patch, temporal, w.stride(0), _ptr(out), ld_out,
+                                     DTYPES[dt], _stream(stream)))
     return out
 
 
@@ -131,12 +164,19 @@ def _dev(a: np.ndarray, dtype: str, device, matrix: bool) -> torch.Tensor:
 
 
 class VisionWeights:
-    """Device copies of the tower parameters and the ctypes struct pointing at them."""
+    """Device copies of the tower parameters and the ctypes struct pointing at
+    them.  fold: the Conv3d patch-embed weight is folded on the device into
+    the Conv2d weight of still images (qv_fold_patch_weight)."""
 
-    def __init__(self, params: Dict[str, np.ndarray], depth: int, dtype: str = "bf16", device="cuda"):
+    def __init__(self, params: Dict[str, np.ndarray], depth: int, dtype: str = "bf16", device="cuda",
+                 fold: bool = False):
         self.tensors: Dict[str, torch.Tensor] = {}
         pw = params["patch_w"]
         self.tensors["patch_w"] = _dev(pw.reshape(pw.shape[0], -1), dtype, device, True)
+        if fold:
+            _, c, t, p, _ = pw.shape
+            self.tensors["patch_w_conv3d"] = self.tensors["patch_w"]
+            self.tensors["patch_w"] = fold_patch_weight(self.tensors["patch_w"], c, p, t)
         self.patch_b = None
         if "patch_b" in params:
             self.patch_b = _dev(params["patch_b"], dtype, device, False)
@@ -214,7 +254,8 @@ class Encoder:
 
     def __init__(self, params: Dict[str, np.ndarray], images: Sequence[np.ndarray], depth: int, out_dim: int,
                  dtype: str = "bf16", dim: int = 1280, heads: int = 16, mlp: int = 5120, ln_eps: float = 1e-6,
-                 rope_theta: float = 1e4, window: int = 0, full_blocks=(), device="cuda", grids=None, **grid_kw):
+                 rope_theta: float = 1e4, window: int = 0, full_blocks=(), device="cuda", grids=None,
+                 fold: bool = False, normalize=None, **grid_kw):
         self.dtype = dtype
         self.grid_kw = grid_kw
         if grids is None:
@@ -229,12 +270,13 @@ class Encoder:
         self.cu_host = cu
         self.cu = torch.from_numpy(cu).to(device)
         self.n = int(cu[-1])
-        pd = images[0].shape[1] * 2 * 14 * 14
+        self.fold, self.normalize = fold, normalize
+        pd = patch_width(images[0].shape[1], fold)
         self.vcfg = VisionConfig(depth=depth, dim=dim, heads=heads, mlp=mlp, patch_dim=pd, ld=pd, dtype=dtype,
                                  ln_eps=ln_eps, rope_theta=rope_theta, window=window,
                                  full_blocks=tuple(full_blocks))
         self.mcfg = MergerConfig(dim=dim, out_dim=out_dim, dtype=dtype, ln_eps=ln_eps)
-        self.vw = VisionWeights(params, depth, dtype, device)
+        self.vw = VisionWeights(params, depth, dtype, device, fold=fold)
         self.mw = MergerWeights(params, dtype, device)
         self.patches = torch.empty((self.n, pd), dtype=TORCH_DTYPES[dtype], device=device)
         self.hidden = torch.empty((self.n, dim), dtype=torch.float32, device=device)
@@ -243,7 +285,8 @@ class Encoder:
                                   merge_workspace_size(self.mcfg, self.n)), dtype=torch.uint8, device=device)
 
     def run(self, stream=None):
-        patchify(self.pixels, self.descs, self.grids, self.dtype, out=self.patches, stream=stream, **self.grid_kw)
+        patchify(self.pixels, self.descs, self.grids, self.dtype, out=self.patches, stream=stream, fold=self.fold,
+                 normalize=self.normalize, **self.grid_kw)
         vision_forward(self.vcfg, self.vw, self.patches, self.grids, self.cu, hidden=self.hidden, ws=self.ws,
                        stream=stream)
         patch_merge(self.mcfg, self.mw, self.hidden, out=self.out, ws=self.ws, stream=stream)

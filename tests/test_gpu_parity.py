@@ -178,14 +178,16 @@ def test_deterministic_bitwise():
 
 
 # ------------------------------------------------------- full-size workloads
-def test_full_448_end_to_end():
-    """One 448x448 image through all 32 blocks and the merger, oracle end to end."""
+@pytest.mark.parametrize("fold", [False, True], ids=["conv3d", "conv2d_fold"])
+def test_full_448_end_to_end(fold):
+    """One 448x448 image through all 32 blocks and the merger, oracle end to
+    end (the oracle always takes the Conv3d definition)."""
     qv = _qv()
     wl = synth.W448
-    _say(f"{wl.name}: drawing params")
+    _say(f"{wl.name} fold={fold}: drawing params")
     params = synth.params(wl)
     imgs = synth.pixels(wl)
-    enc = qv.Encoder(params, imgs, depth=wl.depth, out_dim=wl.out_dim, dtype=wl.dtype)
+    enc = qv.Encoder(params, imgs, depth=wl.depth, out_dim=wl.out_dim, dtype=wl.dtype, fold=fold)
     enc.run()
     torch.cuda.synchronize()
     grids = [O.grid_thw(h, w, f)[2] for h, w, f in wl.images]
@@ -211,17 +213,18 @@ FULL = ["qwen2vl_2b_672x4_varlen", "mixed16_varlen_7b_merger", "maxres_3584", "q
 
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_sampled(name):
-    """Full-size workload in the benchmark's launch configuration: exact
-    patchify and metadata; first and last block teacher-forced on sampled
-    rows; merger on sampled groups."""
+    """Full-size workload in the benchmark's launch configuration (still
+    images take the Conv2d fold there): exact patchify and metadata; first
+    and last block teacher-forced on sampled rows; merger on sampled groups."""
     qv = _qv()
     wl = synth.WORKLOADS[name]
     _say(f"{name}: drawing inputs")
     params = synth.params(wl)
     imgs = synth.pixels(wl)
     grids = [O.grid_thw(h, w, f)[2] for h, w, f in wl.images]
+    fold = all(f == 1 for _, _, f in wl.images)
     enc = qv.Encoder(params, imgs, depth=wl.depth, out_dim=wl.out_dim, dtype=wl.dtype, window=wl.window,
-                     full_blocks=wl.full_blocks)
+                     full_blocks=wl.full_blocks, fold=fold)
     assert enc.grids == [tuple(g) for g in grids]
     cu, pos, _ = O.seq_meta(grids)
     windows = O.window_groups(grids, wl.window) if wl.window else None
@@ -230,7 +233,7 @@ def test_full_size_sampled(name):
     enc.run()
     torch.cuda.synchronize()
     # patch matrix: bit-exact against the oracle's gather + RNE cast
-    x_ref = O.patchify(imgs, grids)
+    x_ref = O.patchify_folded(imgs, grids, width=592) if fold else O.patchify(imgs, grids)
     assert np.array_equal(enc.patches.view(torch.int16).cpu().numpy().view(np.uint16), O.bf16_round(x_ref))
     del x_ref
     out_full = _host(enc.out)

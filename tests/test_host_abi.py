@@ -145,6 +145,35 @@ def test_patchify_validation():
     assert L.qv_patchify(FAKE, imgs, 1, g.ctypes.data, None, FAKE, _abi.QV_BF16, 1176, None) == _abi.QV_ERR_SHAPE
 
 
+def test_patchify_ex_and_fold_validation():
+    L = qv.lib()
+    g = np.array([[1, 4, 4]], np.int32)
+    imgs = (_abi.Image * 1)(_abi.Image(0, 1, 3, 56, 56, 0))
+    opts = qv.patch_opts(fold=True, normalize=True)
+    ok = L.qv_patchify_ex  # validation only below: every call fails before a launch
+    assert ok(FAKE, imgs, 1, g.ctypes.data, None, ctypes.byref(opts), FAKE, _abi.QV_BF16, 584, None) == \
+        _abi.QV_ERR_SHAPE                                               # folded rows are 592 wide
+    imgs[0].frames = 2                                                  # two frames: nothing to fold
+    g2 = np.array([[1, 4, 4]], np.int32)
+    assert ok(FAKE, imgs, 1, g2.ctypes.data, None, ctypes.byref(opts), FAKE, _abi.QV_BF16, 592, None) == \
+        _abi.QV_ERR_SHAPE
+    imgs[0].frames = 1
+    bad = qv.patch_opts(normalize=((0.5, 0.5, 0.5), (0.2, 0.0, 0.2)))  # std 0
+    assert ok(FAKE, imgs, 1, g.ctypes.data, None, ctypes.byref(bad), FAKE, _abi.QV_BF16, 1176, None) == \
+        _abi.QV_ERR_UNSUPPORTED
+    flag = qv.patch_opts()
+    flag.fold = 2
+    assert ok(FAKE, imgs, 1, g.ctypes.data, None, ctypes.byref(flag), FAKE, _abi.QV_BF16, 1176, None) == \
+        _abi.QV_ERR_UNSUPPORTED
+    assert ok(None, imgs, 1, g.ctypes.data, None, None, FAKE, _abi.QV_BF16, 1176, None) == _abi.QV_ERR_NULL
+    F = L.qv_fold_patch_weight
+    assert F(FAKE, 1280, 3, 14, 2, 1176, None, 592, _abi.QV_BF16, None) == _abi.QV_ERR_NULL
+    assert F(FAKE, 1280, 3, 14, 2, 1170, FAKE, 592, _abi.QV_BF16, None) == _abi.QV_ERR_SHAPE
+    assert F(FAKE, 1280, 3, 14, 2, 1176, FAKE, 580, _abi.QV_BF16, None) == _abi.QV_ERR_SHAPE
+    assert F(FAKE, 1280, 3, 14, 2, 1176, FAKE, 592, 9, None) == _abi.QV_ERR_UNSUPPORTED
+    assert qv.patch_width(3, fold=True) == 592 and qv.patch_width(3) == 1176
+
+
 def test_merge_validation():
     L = qv.lib()
     w = _abi.MergerW(*([0x2000] * 6))
