@@ -96,13 +96,17 @@ def _workloads() -> Dict[str, Workload]:
         full_blocks=(7, 15, 23, 31),
         description="one 3584x3584 image, 256x256 grid, 32 blocks attending in 8x8-patch windows "
                     "except blocks 7/15/23/31, merger to 3584, bf16")
-    return {w.name: w for w in (toy, w448, w672x4, mixed, maxres, maxres_win)}
+    video = Workload(
+        name="video_448_16f", images=((448, 448, 16),), depth=32,
+        description="one 16-frame 448x448 clip (8 temporal patches of distinct frame pairs, one attention "
+                    "segment), 32 blocks, merger to 1536, bf16")
+    return {w.name: w for w in (toy, w448, w672x4, mixed, maxres, maxres_win, video)}
 
 
 WORKLOADS: Dict[str, Workload] = _workloads()
-TOY, W448, W672X4, MIXED16, MAXRES, MAXRES_WIN = (
+TOY, W448, W672X4, MIXED16, MAXRES, MAXRES_WIN, VIDEO16 = (
     WORKLOADS[k] for k in ("toy_112_fp32", "qwen2vl_2b_448", "qwen2vl_2b_672x4_varlen", "mixed16_varlen_7b_merger",
-                           "maxres_3584", "qwen25vl_7b_3584_window"))
+                           "maxres_3584", "qwen25vl_7b_3584_window", "video_448_16f"))
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:

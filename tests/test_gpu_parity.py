@@ -208,7 +208,8 @@ def _sampled_rows(cu, rng, per_image=4):
     return np.unique(np.asarray(rows))
 
 
-FULL = ["qwen2vl_2b_672x4_varlen", "mixed16_varlen_7b_merger", "maxres_3584", "qwen25vl_7b_3584_window"]
+FULL = ["qwen2vl_2b_672x4_varlen", "mixed16_varlen_7b_merger", "maxres_3584", "qwen25vl_7b_3584_window",
+        "video_448_16f"]
 
 
 @pytest.mark.parametrize("name", FULL)

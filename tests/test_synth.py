@@ -18,7 +18,7 @@ def test_mixed_batch_draw():
 def test_workload_token_counts():
     want = {"toy_112_fp32": (64, 16), "qwen2vl_2b_448": (1024, 256), "qwen2vl_2b_672x4_varlen": (9216, 2304),
             "mixed16_varlen_7b_merger": (39692, 9923), "maxres_3584": (65536, 16384),
-            "qwen25vl_7b_3584_window": (65536, 16384)}
+            "qwen25vl_7b_3584_window": (65536, 16384), "video_448_16f": (8192, 2048)}
     for name, wl in synth.WORKLOADS.items():
         grids = [O.grid_thw(h, w, f)[2] for h, w, f in wl.images]
         n = sum(t * gh * gw for t, gh, gw in grids)
