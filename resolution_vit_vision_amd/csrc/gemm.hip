@@ -159,6 +159,33 @@ struct EpiStoreF32 {
   }
 };
 
+// Split-K partial sums: run s of the K range stores its float32 tile (no
+// bias) at C + s * stride; the sum over the runs, the bias and the residual
+// are added later in a fixed order (launch_layernorm_acc).
+struct EpiPartF32 {
+  static constexpr bool kStaged = true;
+  static constexpr int kPatchFloats = 32 * 40;
+  using RowParam = NoRowParam;
+  static constexpr int kRowParamFloats = 0;
+  float* C; int ldc; size_t stride;
+  __device__ float col_param(int) const { return 0.f; }
+  __device__ float pre(float, float v) const { return v; }
+  __device__ RowParam row_param(int, int) const { return {}; }
+  __device__ void store(int row, int col, const float (&v)[4], const RowParam&) const {
+    *reinterpret_cast<float4*>(C + (size_t)row * ldc + col) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+  template <int FM, int FN>
+  __device__ void apply_staged(f32x16 (&acc)[FM][FN], float* wlds, int wm0, int wn0, int lane, int M, int N) const {
+    staged_store<4>(*this, acc, wlds, wm0, wn0, lane, M, N);
+  }
+};
+
+__device__ __forceinline__ EpiPartF32 epi_at_split(const EpiPartF32& e, int s) {
+  EpiPartF32 r = e;
+  r.C += (size_t)s * e.stride;
+  return r;
+}
+
 struct EpiResidF32 {
   static constexpr bool kStaged = true;
   static constexpr int kPatchFloats = 32 * 40;
@@ -600,9 +627,11 @@ static hipError_t launch_pipe(const void* A, int lda, const void* B, int ldb, in
 
 template <int BM, int BN, int WM, int WN, int ST, int KT, int NP, class Epi, class RowMap>
 static hipError_t launch_ws(const void* A, int lda, const void* B, int ldb, int M, int N, const Epi& epi,
-                            RowMap rmap, hipStream_t s) {
+                            RowMap rmap, hipStream_t s, int splits = 1) {
   const XcdCut cut = xcd_cut((M + BM - 1) / BM, (N + BN - 1) / BN, BM, BN);
-  hipLaunchKernelGGL((k_gemm_ws<BM, BN, WM, WN, ST, KT, NP, Epi, RowMap>), dim3(cut.grid), dim3((WM * WN + NP) * 64), 0,
+  // the grid width is a multiple of 8, so workgroup (x, y) still runs on XCD x % 8
+  hipLaunchKernelGGL((k_gemm_ws<BM, BN, WM, WN, ST, KT, NP, Epi, RowMap>), dim3(cut.grid, (unsigned)splits),
+                     dim3((WM * WN + NP) * 64), 0,
                      s, reinterpret_cast<const uint16_t*>(A), lda, reinterpret_cast<const uint16_t*>(B), ldb, M, N,
                      cut.xgn, 8, epi, rmap);
   return hipGetLastError();
@@ -664,6 +693,33 @@ hipError_t gemm_bf16_store_f32(const void* A, int lda, const void* B, int ldb, i
 hipError_t gemm_bf16_resid_f32(const void* A, int lda, const void* B, int ldb, int M, int N, int K,
                                const float* bias, float* Z, int ldz, hipStream_t s) {
   return run_bf16(A, lda, B, ldb, M, N, K, EpiResidF32{Z, ldz, bias}, RowMapIdentity{}, s);
+}
+
+// Split-K for narrow outputs at small M: 128x160 tiles (warp-specialized)
+// with the K range cut into `splits` runs, one workgroup per (tile, run),
+// so the grid fills the 256 CUs where the plain tiling has 64 tiles.
+int gemm_splitk_runs(int M, int N, int K) {
+  if (N % 160 || K % 64) return 1;
+  const int64_t tiles = (int64_t)((M + 127) / 128) * (N / 160);
+  for (int s : {4, 2}) {
+    const int kt = K / 64 / s;
+    if ((K / 64) % s == 0 && tiles * s <= 256 && (kt == 20 || kt == 5 || kt == 40 || kt == 10)) return s;
+  }
+  return 1;
+}
+
+hipError_t gemm_bf16_splitk_f32(const void* A, int lda, const void* B, int ldb, int M, int N, int K, int splits,
+                                float* P, hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (splits < 1 || N % 160 || K % 64 || (K / 64) % splits || lda % 8 || ldb % 8) return hipErrorInvalidValue;
+  const EpiPartF32 e{P, N, (size_t)M * N};
+  switch (K / 64 / splits) {
+    case 20: return launch_ws<128, 160, 4, 1, 4, 20, 4>(A, lda, B, ldb, M, N, e, RowMapIdentity{}, s, splits);
+    case 40: return launch_ws<128, 160, 4, 1, 4, 40, 4>(A, lda, B, ldb, M, N, e, RowMapIdentity{}, s, splits);
+    case 10: return launch_ws<128, 160, 4, 1, 4, 10, 4>(A, lda, B, ldb, M, N, e, RowMapIdentity{}, s, splits);
+    case 5: return launch_ws<128, 160, 4, 1, 4, 5, 4>(A, lda, B, ldb, M, N, e, RowMapIdentity{}, s, splits);
+    default: return hipErrorInvalidValue;
+  }
 }
 hipError_t gemm_bf16_act_bf16(const void* A, int lda, const void* B, int ldb, int M, int N, int K,
                               const float* bias, Act act, void* C, int ldc, hipStream_t s) {

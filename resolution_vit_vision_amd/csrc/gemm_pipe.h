@@ -348,10 +348,19 @@ struct WsConsumer {
   }
 };
 
+// Split-K: workgroup row blockIdx.y multiplies the y-th run of KT * 64
+// columns of A and B, and its epilogue is the one epi_at_split() derives for
+// that run (a partial-sum epilogue writes its own slice; every other
+// epilogue is used as is, with one run).
+template <class E>
+__device__ __forceinline__ E epi_at_split(const E& e, int) {
+  return e;
+}
+
 template <int BM, int BN, int WM, int WN, int STAGES, int KT, int NP, class Epi, class RowMap>
 __global__ __launch_bounds__((WM * WN + NP) * 64) void k_gemm_ws(const uint16_t* __restrict__ A, int lda,
                                                                 const uint16_t* __restrict__ B, int ldb, int M,
-                                                                int N, int xgn, int group, Epi epi, RowMap rmap) {
+                                                                int N, int xgn, int group, Epi epi_all, RowMap rmap) {
   using C = PipeCfg<BM, BN, WM, WN, STAGES, 1>;
   constexpr int NC = WM * WN;
   constexpr int BLOCKS = (BM + BN) * 8 / 64;  // 1 KB blocks per stage
@@ -375,6 +384,9 @@ __global__ __launch_bounds__((WM * WN + NP) * 64) void k_gemm_ws(const uint16_t*
   int tm, tn;
   if (!tile_coords(blockIdx.x, tiles_m, tiles_n, xgn, group, tm, tn)) return;  // uniform over the workgroup
   const int m0 = tm * BM, n0 = tn * BN;
+  A += (size_t)blockIdx.y * KT * 64;
+  B += (size_t)blockIdx.y * KT * 64;
+  const Epi epi = epi_at_split(epi_all, (int)blockIdx.y);
 
   if (wave >= NC) {
     const char* gsrc[LP];

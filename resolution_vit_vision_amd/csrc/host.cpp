@@ -318,12 +318,13 @@ struct VisionPlan {
   std::vector<ImgDesc> desc;
   std::vector<PlanEntry> plan;
   // windowed attention: a second padded layout with one kSeqAlign-row slot per window
+  int split_proj = 1, split_fc2 = 1;  // split-K runs of the out-projection and fc2 (bf16, small M)
   int window = 0;
   int64_t n_win = 0, Pw = 0;
   int total_qtiles_w = 0;
   std::vector<PlanEntry> plan_w;
   size_t off_tok = 0, off_plan = 0, off_rope = 0, off_a = 0, off_q = 0, off_k = 0, off_vt = 0, off_vt_end = 0,
-         off_o = 0, off_h = 0, off_qkv = 0, off_tokw = 0, off_outrow = 0, off_planw = 0, total = 0;
+         off_o = 0, off_h = 0, off_qkv = 0, off_tokw = 0, off_outrow = 0, off_planw = 0, off_part = 0, total = 0;
 };
 
 qv_status check_vision_cfg(const qv_vision_cfg* c) {
@@ -434,6 +435,13 @@ qv_status make_plan(const qv_vision_cfg* c, const int32_t* grid_thw, int32_t n_i
   vp.off_h = o;    o = align_up(o + N * c->mlp * es);
   vp.off_qkv = o;
   if (c->dtype == QV_F32) o = align_up(o + N * 3 * c->dim * sizeof(float));
+  if (c->dtype == QV_BF16 && c->dim == 1280 && c->depth > 0) {
+    vp.split_proj = gemm_splitk_runs((int)N, c->dim, c->dim);
+    vp.split_fc2 = gemm_splitk_runs((int)N, c->dim, c->mlp);
+  }
+  const int parts = std::max(vp.split_proj, vp.split_fc2);
+  vp.off_part = o;
+  if (parts > 1) o = align_up(o + (size_t)parts * N * c->dim * sizeof(float));
   if (vp.window) {
     vp.off_tokw = o;   o = align_up(o + N * sizeof(int2));
     vp.off_outrow = o; o = align_up(o + (size_t)vp.Pw * sizeof(int32_t));
@@ -551,6 +559,25 @@ qv_status qv_vision_forward(const qv_vision_cfg* c, const qv_vision_w* w, const 
   std::unique_lock<std::mutex> warm_lock;
   if (wc) warm_lock = std::unique_lock<std::mutex>(wc->mu);
   const size_t wb = 2;  // bf16 weights
+  // Split-K (small M): the out-projection and fc2 leave float32 partial sums;
+  // the LayerNorm that follows adds them, the bias and the residual in a
+  // fixed order (after the last block a residual-only pass does it).
+  float* part = reinterpret_cast<float*>(base + vp.off_part);
+  const size_t part_stride = (size_t)vp.N * c->dim;
+  int pending = 0;
+  const float* pending_bias = nullptr;
+  auto layer_norm = [&](const void* g, const void* bta) -> qv_status {
+    if (pending) {
+      QV_LAUNCH(QV_KC_LAYERNORM, s, launch_layernorm_acc(hidden, part, part_stride, pending, pending_bias,
+                                                         (const float*)g, (const float*)bta, A, bf, (int)vp.N,
+                                                         c->dim, c->ln_eps, s));
+      pending = 0;
+    } else {
+      QV_LAUNCH(QV_KC_LAYERNORM, s, launch_layernorm(hidden, (const float*)g, (const float*)bta, A, bf, (int)vp.N,
+                                                     c->dim, c->ln_eps, s));
+    }
+    return QV_OK;
+  };
   for (int l = 0; l < c->depth; ++l) {
     const qv_block_w& b = w->blocks[l];
     if (wc) {
@@ -565,11 +592,18 @@ qv_status qv_vision_forward(const qv_vision_cfg* c, const qv_vision_w* w, const 
     const bool win = vp.window && !(l < 64 && ((c->full_blocks >> l) & 1u));
     const QkvOut& qb = win ? qow : qo;
     const AttnArgs& ab = win ? aw : aa;
-    QV_LAUNCH(QV_KC_LAYERNORM, s, launch_layernorm(hidden, (const float*)b.ln1_w, (const float*)b.ln1_b, A, bf, M, D, c->ln_eps, s));
+    qv_status lst = layer_norm(b.ln1_w, b.ln1_b);
+    if (lst != QV_OK) return lst;
     if (bf) {
       QV_LAUNCH(QV_KC_QKV, s, gemm_bf16_qkv(A, D, b.qkv_w, D, M, D, (const float*)b.qkv_b, qb, s));
       QV_LAUNCH(QV_KC_ATTENTION, s, attention_bf16(ab, s));
-      QV_LAUNCH(QV_KC_PROJ, s, gemm_bf16_resid_f32(O, D, b.proj_w, D, M, D, D, (const float*)b.proj_b, hidden, D, s));
+      if (vp.split_proj > 1) {
+        QV_LAUNCH(QV_KC_PROJ, s, gemm_bf16_splitk_f32(O, D, b.proj_w, D, M, D, D, vp.split_proj, part, s));
+        pending = vp.split_proj;
+        pending_bias = (const float*)b.proj_b;
+      } else {
+        QV_LAUNCH(QV_KC_PROJ, s, gemm_bf16_resid_f32(O, D, b.proj_w, D, M, D, D, (const float*)b.proj_b, hidden, D, s));
+      }
     } else {
       float* qkv = reinterpret_cast<float*>(base + vp.off_qkv);
       QV_LAUNCH(QV_KC_QKV, s, gemm_f32_store((const float*)A, D, (const float*)b.qkv_w, D, M, 3 * D, D, (const float*)b.qkv_b, qkv,
@@ -579,16 +613,28 @@ qv_status qv_vision_forward(const qv_vision_cfg* c, const qv_vision_w* w, const 
       QV_LAUNCH(QV_KC_PROJ, s, gemm_f32_resid((const float*)O, D, (const float*)b.proj_w, D, M, D, D, (const float*)b.proj_b, hidden,
                             D, s));
     }
-    QV_LAUNCH(QV_KC_LAYERNORM, s, launch_layernorm(hidden, (const float*)b.ln2_w, (const float*)b.ln2_b, A, bf, M, D, c->ln_eps, s));
+    lst = layer_norm(b.ln2_w, b.ln2_b);
+    if (lst != QV_OK) return lst;
     if (bf) {
       QV_LAUNCH(QV_KC_FC1, s, gemm_bf16_act_bf16(A, D, b.fc1_w, D, M, F, D, (const float*)b.fc1_b, Act::QuickGelu, H, F, s));
-      QV_LAUNCH(QV_KC_FC2, s, gemm_bf16_resid_f32(H, F, b.fc2_w, F, M, D, F, (const float*)b.fc2_b, hidden, D, s));
+      if (vp.split_fc2 > 1) {
+        QV_LAUNCH(QV_KC_FC2, s, gemm_bf16_splitk_f32(H, F, b.fc2_w, F, M, D, F, vp.split_fc2, part, s));
+        pending = vp.split_fc2;
+        pending_bias = (const float*)b.fc2_b;
+      } else {
+        QV_LAUNCH(QV_KC_FC2, s, gemm_bf16_resid_f32(H, F, b.fc2_w, F, M, D, F, (const float*)b.fc2_b, hidden, D, s));
+      }
     } else {
       QV_LAUNCH(QV_KC_FC1, s, gemm_f32_act((const float*)A, D, (const float*)b.fc1_w, D, M, F, D, (const float*)b.fc1_b,
                           Act::QuickGelu, (float*)H, F, s));
       QV_LAUNCH(QV_KC_FC2, s, gemm_f32_resid((const float*)H, F, (const float*)b.fc2_w, F, M, D, F, (const float*)b.fc2_b, hidden, D,
                             s));
     }
+  }
+  if (pending) {
+    QV_LAUNCH(QV_KC_LAYERNORM, s, launch_layernorm_acc(hidden, part, part_stride, pending, pending_bias, nullptr,
+                                                       nullptr, nullptr, bf, (int)vp.N, c->dim, c->ln_eps, s));
+    pending = 0;
   }
   if (wc) {
     QV_HIP(hipEventRecord(wc->done, wc->side));

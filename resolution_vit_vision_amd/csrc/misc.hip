@@ -319,6 +319,101 @@ __global__ __launch_bounds__(256) void k_layernorm(const float* __restrict__ x, 
   }
 }
 
+// Residual update from split-K partial sums, then LayerNorm of the result:
+// x = x + ((p_0 + p_1 + ... + p_{S-1}) + pb), summed in that order, written
+// back; then y = LN(x) as in k_layernorm when g is non-null.  Same one
+// memory round trip: the row, the S partial rows, pb, g and b are loaded up
+// front.
+template <int NV, int S>
+__global__ __launch_bounds__(256) void k_layernorm_acc(float* __restrict__ x, const float* __restrict__ parts,
+                                                       size_t part_stride, const float* __restrict__ pb,
+                                                       const float* __restrict__ g, const float* __restrict__ b,
+                                                       void* __restrict__ y, int bf16, int rows, float eps) {
+  constexpr int D = NV * 256;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  float4* xr = reinterpret_cast<float4*>(x + (size_t)row * D);
+  float4 v[NV], acc[NV], bias[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) v[i] = xr[i * 64 + lane];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) acc[i] = reinterpret_cast<const float4*>(parts + (size_t)row * D)[i * 64 + lane];
+  float4 pp[S - 1][NV];
+#pragma unroll
+  for (int k = 1; k < S; ++k)
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      pp[k - 1][i] = reinterpret_cast<const float4*>(parts + k * part_stride + (size_t)row * D)[i * 64 + lane];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) bias[i] = reinterpret_cast<const float4*>(pb)[i * 64 + lane];
+  float4 gg[NV], bb[NV];
+  if (g) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      gg[i] = reinterpret_cast<const float4*>(g)[i * 64 + lane];
+      bb[i] = reinterpret_cast<const float4*>(b)[i * 64 + lane];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < S - 1; ++k)
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      acc[i].x += pp[k][i].x; acc[i].y += pp[k][i].y; acc[i].z += pp[k][i].z; acc[i].w += pp[k][i].w;
+    }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    v[i].x += acc[i].x + bias[i].x; v[i].y += acc[i].y + bias[i].y;
+    v[i].z += acc[i].z + bias[i].z; v[i].w += acc[i].w + bias[i].w;
+    xr[i * 64 + lane] = v[i];
+  }
+  if (!g) return;
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) sum += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
+  const float mean = sum * (1.0f / D);
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    v[i].x -= mean; v[i].y -= mean; v[i].z -= mean; v[i].w -= mean;
+    sq += (v[i].x * v[i].x + v[i].y * v[i].y) + (v[i].z * v[i].z + v[i].w * v[i].w);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
+  const float rstd = rsqrtf(sq * (1.0f / D) + eps);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const float o0 = v[i].x * rstd * gg[i].x + bb[i].x, o1 = v[i].y * rstd * gg[i].y + bb[i].y;
+    const float o2 = v[i].z * rstd * gg[i].z + bb[i].z, o3 = v[i].w * rstd * gg[i].w + bb[i].w;
+    if (bf16) {
+      uint2 pk;
+      pk.x = f32_to_bf16_rne(o0) | ((uint32_t)f32_to_bf16_rne(o1) << 16);
+      pk.y = f32_to_bf16_rne(o2) | ((uint32_t)f32_to_bf16_rne(o3) << 16);
+      reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(y) + (size_t)row * D)[i * 64 + lane] = pk;
+    } else {
+      reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + (size_t)row * D)[i * 64 + lane] =
+          make_float4(o0, o1, o2, o3);
+    }
+  }
+}
+
+hipError_t launch_layernorm_acc(float* x, const float* parts, size_t part_stride, int splits, const float* pb,
+                                const float* g, const float* b, void* y, bool bf16, int rows, int dim, float eps,
+                                hipStream_t s) {
+  if (dim != 1280) return hipErrorInvalidValue;
+  dim3 grid((unsigned)((rows + 3) / 4));
+  switch (splits) {
+    case 2: hipLaunchKernelGGL((k_layernorm_acc<5, 2>), grid, dim3(256), 0, s, x, parts, part_stride, pb, g, b, y,
+                               bf16 ? 1 : 0, rows, eps); break;
+    case 4: hipLaunchKernelGGL((k_layernorm_acc<5, 4>), grid, dim3(256), 0, s, x, parts, part_stride, pb, g, b, y,
+                               bf16 ? 1 : 0, rows, eps); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_layernorm(const float* x, const float* g, const float* b, void* y, bool bf16, int rows, int dim,
                             float eps, hipStream_t s) {
   dim3 grid((unsigned)((rows + 3) / 4));

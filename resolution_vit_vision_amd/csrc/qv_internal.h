@@ -107,6 +107,16 @@ hipError_t gemm_bf16_store_f32(const void* A, int lda, const void* B, int ldb, i
                                const float* bias, float* C, int ldc, hipStream_t s);
 hipError_t gemm_bf16_resid_f32(const void* A, int lda, const void* B, int ldb, int M, int N, int K,
                                const float* bias, float* Z, int ldz, hipStream_t s);
+// Split-K with the reduction left to launch_layernorm_acc: returns the number
+// of K runs that fills the GPU for this shape (1 = no split).
+int gemm_splitk_runs(int M, int N, int K);
+// P[s][M][N] = A[:, s K/S .. (s+1) K/S) . B[:, same]^T, float32, no bias.
+hipError_t gemm_bf16_splitk_f32(const void* A, int lda, const void* B, int ldb, int M, int N, int K, int splits,
+                                float* P, hipStream_t s);
+// x += sum_s parts[s] + pb (in that order); y = LN(x) if g is non-null.
+hipError_t launch_layernorm_acc(float* x, const float* parts, size_t part_stride, int splits, const float* pb,
+                                const float* g, const float* b, void* y, bool bf16, int rows, int dim, float eps,
+                                hipStream_t s);
 hipError_t gemm_bf16_act_bf16(const void* A, int lda, const void* B, int ldb, int M, int N, int K,
                               const float* bias, Act act, void* C, int ldc, hipStream_t s);
 hipError_t gemm_bf16_qkv(const void* A, int lda, const void* B, int ldb, int M, int K, const float* bias,
