@@ -229,7 +229,10 @@ typedef struct qv_vision_cfg {
    * windows are truncated; 0 = every block attends over the whole image
    * (Qwen2-VL).  full_blocks: with window > 0, bit l set = block l attends
    * over the whole image (Qwen2.5-VL: bits 7, 15, 23, 31); blocks from 64
-   * on are windowed.  full_blocks is ignored when window is 0. */
+   * on are windowed.  full_blocks is ignored when window is 0.  Workspace:
+   * every window gets a slot of 64 padded rows (W <= 8) or 128 (W = 10) in
+   * the q/k/v layout, so small windows cost more q/k/v workspace than the
+   * image layout (W = 8: none; W = 2: 16x). */
   int32_t window;
   int32_t reserved0;  /* 0 */
   uint64_t full_blocks;

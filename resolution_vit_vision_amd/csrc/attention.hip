@@ -346,6 +346,143 @@ hipError_t attention_bf16(const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ======================================================= small windows
+// Windowed blocks whose windows hold at most 64 patches (W <= 8): one
+// workgroup of two waves per (window, head).  A window sits in a 64-row slot
+// of the padded layout, so its keys are two 32-key tiles of the key-tiled K
+// (10 KB, contiguous) and 64 columns of V^T (80 rows of 128 B, 16-byte key
+// chunks XOR-swizzled by (row >> 1) & 7): one LDS-DMA round brings all of it.
+// Each wave takes 32 queries, forms both score tiles with the same MFMA
+// layout as the full-attention kernel, and runs an exact softmax over the 64
+// scores of each query (no running max, no rescale); P.V again pads the head
+// to 96 rows with row 80 a row of ones for the denominator.
+__global__ __launch_bounds__(128) void k_attn_win(AttnArgs a, float scale_log2) {
+  constexpr int K_BYTES = 2 * 32 * kHeadDim * 2;   // 10240
+  constexpr int V_BYTES = kHeadDim * kWinSlot * 2;  // 10240
+  constexpr int BLKS = (K_BYTES + V_BYTES) / 1024;  // 20 DMA blocks, 10 per wave
+  __shared__ __attribute__((aligned(1024))) char lds[K_BYTES + V_BYTES];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hlf = lane >> 5, l32 = lane & 31;
+  const int head = blockIdx.x % a.heads, win = blockIdx.x / a.heads;
+  const PlanEntry pe = a.plan[win];  // window order
+  const int n = pe.n;
+
+  const char* Kt = reinterpret_cast<const char*>(a.k) + kc_offset(head, a.P, pe.prow0, 0) * 2;
+  const char* Vh = reinterpret_cast<const char*>(a.vt) + ((size_t)head * kHeadDim * a.P + pe.prow0) * 2;
+#pragma unroll
+  for (int i = 0; i < BLKS / 2; ++i) {
+    const int blk = wave + 2 * i;
+    const int slot = blk * 64 + lane;  // 16-byte slot of the LDS image
+    const char* src;
+    if (slot < K_BYTES / 16) {
+      src = Kt + (size_t)slot * 16;
+    } else {
+      const int sv = slot - K_BYTES / 16;
+      const int d = sv >> 3, p = sv & 7;
+      src = Vh + ((size_t)d * a.P + 8 * (p ^ ((d >> 1) & 7))) * 2;
+    }
+    __builtin_amdgcn_global_load_lds((gas_ptr)src, (las_ptr)(lds + blk * 1024), 16, 0, 0);
+  }
+  const int q0 = 32 * wave;
+  bf16x8 qf[5];
+  {
+    const uint16_t* qr = reinterpret_cast<const uint16_t*>(a.q) +
+                         ((size_t)head * a.P + pe.prow0 + q0 + l32) * kHeadDim + 8 * hlf;
+#pragma unroll
+    for (int kk = 0; kk < 5; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qr + 16 * kk);
+  }
+  QV_WAIT_VM(0);
+  __syncthreads();
+  if (q0 >= n) return;  // no query rows for this wave (after the only barrier)
+
+  f32x16 sc[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const uint16_t* sK = reinterpret_cast<const uint16_t*>(lds + t * (K_BYTES / 2));
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sc[t][r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 5; ++kk)
+      sc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          *reinterpret_cast<const bf16x8*>(sK + ((2 * kk + hlf) * 32 + l32) * 8), qf[kk], sc[t], 0, 0, 0);
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 32 * t + 8 * (r >> 2) + 4 * hlf + (r & 3);
+      if (key >= n) sc[t][r] = -INFINITY;
+      mx = fmaxf(mx, sc[t][r]);
+    }
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  const float msc = mx * scale_log2;  // key 0 is always valid: mx is finite
+  bf16x8 pb[2][2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        pb[t][s2][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[t][8 * s2 + e], scale_log2, -msc));
+
+  bf16x8 vconst;
+  {
+    const __bf16 one = __builtin_bit_cast(__bf16, (uint16_t)(l32 == 16 ? 0x3F80 : 0));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vconst[e] = one;
+  }
+  f32x16 o[3];
+#pragma unroll
+  for (int t = 0; t < 3; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
+  const uint16_t* sV = reinterpret_cast<const uint16_t*>(lds + K_BYTES);
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int chunk = 4 * t + 2 * s2 + hlf;  // 8-key chunk of the 64 keys
+#pragma unroll
+      for (int tt = 0; tt < 3; ++tt) {
+        const int d = 32 * tt + l32;
+        bf16x8 vf;
+        if (tt < 2 || l32 < kHeadDim - 64)
+          vf = *reinterpret_cast<const bf16x8*>(sV + d * kWinSlot + ((chunk ^ ((d >> 1) & 7)) << 3));
+        else
+          vf = vconst;
+        o[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[t][s2], o[tt], 0, 0, 0);
+      }
+    }
+  const float lsum = __shfl(o[2][8], l32, 64);
+  const float inv = 1.0f / lsum;
+  const int q = q0 + l32;
+  if (q < n) {
+    uint16_t* orow = reinterpret_cast<uint16_t*>(a.o) + (size_t)a.out_row[pe.prow0 + q] * a.ldo + head * kHeadDim;
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * t + 8 * g + 4 * hlf;
+        if (d0 < kHeadDim) {
+          uint2 pk;
+          pk.x = pack_bf16(o[t][4 * g] * inv, o[t][4 * g + 1] * inv);
+          pk.y = pack_bf16(o[t][4 * g + 2] * inv, o[t][4 * g + 3] * inv);
+          *reinterpret_cast<uint2*>(orow + d0) = pk;
+        }
+      }
+  }
+}
+
+hipError_t attention_bf16_windows(const AttnArgs& a, hipStream_t s) {
+  if (a.n_img == 0) return hipSuccess;
+  if (a.P % kWinSlot || !a.out_row) return hipErrorInvalidValue;
+  const float scale_log2 = 1.4426950408889634f / sqrtf((float)kHeadDim);
+  hipLaunchKernelGGL(k_attn_win, dim3((unsigned)a.n_img * (unsigned)a.heads), dim3(128), 0, s, a, scale_log2);
+  return hipGetLastError();
+}
+
 // ============================================================ float32 mode
 // One wave per (64 query rows, head); one query row per lane with the full
 // head vector and accumulator in registers; 32-key tiles in LDS; exact exp.

@@ -320,6 +320,7 @@ struct VisionPlan {
   // windowed attention: a second padded layout with one kSeqAlign-row slot per window
   int split_proj = 1, split_fc2 = 1;  // split-K runs of the out-projection and fc2 (bf16, small M)
   int window = 0;
+  int win_slot = 0;  // padded rows per window: kWinSlot (64) for W <= 8, else kSeqAlign (128)
   int64_t n_win = 0, Pw = 0;
   int total_qtiles_w = 0;
   std::vector<PlanEntry> plan_w;
@@ -389,11 +390,13 @@ qv_status make_plan(const qv_vision_cfg* c, const int32_t* grid_thw, int32_t n_i
   }
   vp.total_qtiles = qt;
   if (c->window > 0) {
-    // windows of at most 10 x 10 patches fit one kSeqAlign-row slot; queries
-    // in tiles of 64 rows (the bf16 kernel's 64-row workgroups read 128-key
-    // stages, exactly one slot)
+    // Every window gets a slot of padded rows: 64 when W <= 8 (the small-window
+    // kernel, one workgroup per window and head, plan in window order), else
+    // 128 (windows of up to 10 x 10 patches: the full-attention kernel with
+    // 64-row q-tiles reading one 128-key stage, plan sorted largest first).
     const int W = c->window;
     vp.window = W;
+    vp.win_slot = W * W <= kWinSlot ? kWinSlot : kSeqAlign;
     std::vector<int> wn;  // window sizes in global window order
     for (int i = 0; i < n_img; ++i) {
       ImgDesc& d = vp.desc[i];
@@ -406,17 +409,18 @@ qv_status make_plan(const qv_vision_cfg* c, const int32_t* grid_thw, int32_t n_i
             wn.push_back(std::min(W, d.gh - wy * W) * std::min(W, d.gw - wx * W));
     }
     vp.n_win = (int64_t)wn.size();
-    vp.Pw = vp.n_win * kSeqAlign;
+    vp.Pw = vp.n_win * vp.win_slot;
     if (vp.Pw > INT32_MAX / 2) return fail(QV_ERR_SHAPE, "batch too large");
     const int bqw = c->dtype == QV_BF16 ? 64 : kAttnBQ_f32;
     std::vector<int> worder((size_t)vp.n_win);
     for (int64_t i = 0; i < vp.n_win; ++i) worder[i] = (int)i;
-    std::stable_sort(worder.begin(), worder.end(), [&](int a, int b) { return wn[a] > wn[b]; });
+    if (vp.win_slot != kWinSlot)
+      std::stable_sort(worder.begin(), worder.end(), [&](int a, int b) { return wn[a] > wn[b]; });
     vp.plan_w.resize((size_t)vp.n_win);
     int qtw = 0;
     for (int64_t k = 0; k < vp.n_win; ++k) {
       const int wi = worder[k];
-      vp.plan_w[k] = PlanEntry{wi, wi * kSeqAlign, qtw, wn[wi]};
+      vp.plan_w[k] = PlanEntry{wi, wi * vp.win_slot, qtw, wn[wi]};
       qtw += (wn[wi] + bqw - 1) / bqw;
     }
     vp.total_qtiles_w = qtw;
@@ -531,7 +535,7 @@ qv_status qv_vision_forward(const qv_vision_cfg* c, const qv_vision_w* w, const 
       dc.count = std::min(kDescChunk, n_img - c0);
       dc.first = c0;
       for (int i = 0; i < dc.count; ++i) dc.d[i] = vp.desc[c0 + i];
-      QV_HIP(launch_setup_windows(dc, vp.window, tokw, outrow, s));
+      QV_HIP(launch_setup_windows(dc, vp.window, vp.win_slot, tokw, outrow, s));
     }
     for (int64_t c0 = 0; c0 < vp.n_win; c0 += kPlanChunk) {
       const int cnt = (int)std::min<int64_t>(kPlanChunk, vp.n_win - c0);
@@ -596,7 +600,10 @@ qv_status qv_vision_forward(const qv_vision_cfg* c, const qv_vision_w* w, const 
     if (lst != QV_OK) return lst;
     if (bf) {
       QV_LAUNCH(QV_KC_QKV, s, gemm_bf16_qkv(A, D, b.qkv_w, D, M, D, (const float*)b.qkv_b, qb, s));
-      QV_LAUNCH(QV_KC_ATTENTION, s, attention_bf16(ab, s));
+      if (win && vp.win_slot == kWinSlot)
+        QV_LAUNCH(QV_KC_ATTENTION, s, attention_bf16_windows(aw, s));
+      else
+        QV_LAUNCH(QV_KC_ATTENTION, s, attention_bf16(ab, s));
       if (vp.split_proj > 1) {
         QV_LAUNCH(QV_KC_PROJ, s, gemm_bf16_splitk_f32(O, D, b.proj_w, D, M, D, D, vp.split_proj, part, s));
         pending = vp.split_proj;

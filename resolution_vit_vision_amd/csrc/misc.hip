@@ -144,10 +144,10 @@ hipError_t launch_setup_tokens(const DescChunk& c, int2* tokinfo, hipStream_t s)
 // Windowed attention layout.  Windows tile each frame's patch grid from the
 // top-left corner in steps of `window` patches (edge windows are truncated);
 // window (t, wy, wx) of image i is global window wbase + (t * nwy + wy) * nwx
-// + wx and occupies padded rows [kSeqAlign * global window, + its size).
+// + wx and occupies padded rows [slot * global window, + its size).
 // Inside a window the tokens keep their packed (merge-group) order: group
 // (bh', bw') of the window's ww/2 groups per row, member q = 2 dy + dx.
-__global__ __launch_bounds__(256) void k_setup_windows(DescChunk c, int window, int2* __restrict__ tokinfo_w,
+__global__ __launch_bounds__(256) void k_setup_windows(DescChunk c, int window, int slot, int2* __restrict__ tokinfo_w,
                                                        int32_t* __restrict__ out_row) {
   const int img = blockIdx.y;
   if (img >= c.count) return;
@@ -165,18 +165,18 @@ __global__ __launch_bounds__(256) void k_setup_windows(DescChunk c, int window, 
   const int hl = h - wy * window, wl = w - wx * window;
   const int local = ((hl >> 1) * (ww >> 1) + (wl >> 1)) * 4 + q;
   const int gwin = d.wbase + (t * d.nwy + wy) * d.nwx + wx;
-  const int prow = gwin * kSeqAlign + local;
+  const int prow = gwin * slot + local;
   tokinfo_w[d.row0 + s] = make_int2(h | (w << 16), prow);
   out_row[prow] = d.row0 + s;
 }
 
-hipError_t launch_setup_windows(const DescChunk& c, int window, int2* tokinfo_w, int32_t* out_row,
+hipError_t launch_setup_windows(const DescChunk& c, int window, int slot, int2* tokinfo_w, int32_t* out_row,
                                 hipStream_t s) {
   int nmax = 0;
   for (int i = 0; i < c.count; ++i) nmax = c.d[i].n > nmax ? c.d[i].n : nmax;
   if (nmax == 0) return hipSuccess;
   dim3 grid((unsigned)((nmax + 255) / 256), (unsigned)c.count);
-  hipLaunchKernelGGL(k_setup_windows, grid, dim3(256), 0, s, c, window, tokinfo_w, out_row);
+  hipLaunchKernelGGL(k_setup_windows, grid, dim3(256), 0, s, c, window, slot, tokinfo_w, out_row);
   return hipGetLastError();
 }
 

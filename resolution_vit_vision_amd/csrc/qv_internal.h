@@ -72,7 +72,7 @@ hipError_t launch_setup_tokens(const DescChunk& c, int2* tokinfo, hipStream_t s)
 // windowed attention: tokinfo_w[row] = {h | w << 16, padded row in the window
 // layout (window index * kSeqAlign + place in the window)} and
 // out_row[padded row] = packed row, for windows of `window` patches
-hipError_t launch_setup_windows(const DescChunk& c, int window, int2* tokinfo_w, int32_t* out_row,
+hipError_t launch_setup_windows(const DescChunk& c, int window, int slot, int2* tokinfo_w, int32_t* out_row,
                                 hipStream_t s);
 hipError_t launch_setup_plan(const PlanEntry* host_plan_chunk, int count, int first, PlanEntry* plan,
                              hipStream_t s);
@@ -149,6 +149,10 @@ struct AttnArgs {
   int rows_per_wg;   // query rows per workgroup of the bf16 kernel (128, 64 or 32)
 };
 hipError_t attention_bf16(const AttnArgs& a, hipStream_t s);
+// Windows of at most kWinSlot patches, each in a kWinSlot-row slot; plan in
+// window order (entry i = window i), out_row required.
+constexpr int kWinSlot = 64;
+hipError_t attention_bf16_windows(const AttnArgs& a, hipStream_t s);
 hipError_t attention_f32(const AttnArgs& a, hipStream_t s);
 int attention_bf16_rows_per_wg(int64_t wgs_at_128);
 constexpr int kAttnBQ_f32 = 64;
