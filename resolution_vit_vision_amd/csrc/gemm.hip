@@ -703,7 +703,7 @@ int gemm_splitk_runs(int M, int N, int K) {
   const int64_t tiles = (int64_t)((M + 127) / 128) * (N / 160);
   for (int s : {4, 2}) {
     const int kt = K / 64 / s;
-    if ((K / 64) % s == 0 && tiles * s <= 256 && (kt == 20 || kt == 5 || kt == 40 || kt == 10)) return s;
+    if ((K / 64) % s == 0 && tiles * s <= 256 && (kt == 20 || kt == 40)) return s;
   }
   return 1;
 }
@@ -716,8 +716,6 @@ hipError_t gemm_bf16_splitk_f32(const void* A, int lda, const void* B, int ldb, 
   switch (K / 64 / splits) {
     case 20: return launch_ws<128, 160, 4, 1, 4, 20, 4>(A, lda, B, ldb, M, N, e, RowMapIdentity{}, s, splits);
     case 40: return launch_ws<128, 160, 4, 1, 4, 40, 4>(A, lda, B, ldb, M, N, e, RowMapIdentity{}, s, splits);
-    case 10: return launch_ws<128, 160, 4, 1, 4, 10, 4>(A, lda, B, ldb, M, N, e, RowMapIdentity{}, s, splits);
-    case 5: return launch_ws<128, 160, 4, 1, 4, 5, 4>(A, lda, B, ldb, M, N, e, RowMapIdentity{}, s, splits);
     default: return hipErrorInvalidValue;
   }
 }

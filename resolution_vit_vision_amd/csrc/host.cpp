@@ -318,7 +318,7 @@ struct VisionPlan {
   std::vector<ImgDesc> desc;
   std::vector<PlanEntry> plan;
   // windowed attention: a second padded layout with one kSeqAlign-row slot per window
-  int split_proj = 1, split_fc2 = 1;  // split-K runs of the out-projection and fc2 (bf16, small M)
+  int split_fc2 = 1;  // split-K runs of fc2 (bf16, small M)
   int window = 0;
   int win_slot = 0;  // padded rows per window: kWinSlot (64) for W <= 8, else kSeqAlign (128)
   int64_t n_win = 0, Pw = 0;
@@ -440,12 +440,13 @@ qv_status make_plan(const qv_vision_cfg* c, const int32_t* grid_thw, int32_t n_i
   vp.off_qkv = o;
   if (c->dtype == QV_F32) o = align_up(o + N * 3 * c->dim * sizeof(float));
   if (c->dtype == QV_BF16 && c->dim == 1280 && c->depth > 0) {
-    vp.split_proj = gemm_splitk_runs((int)N, c->dim, c->dim);
+    // fc2 only: the out-projection's K = 1280 is too short for its split to
+    // pay for the partial sums the LayerNorm reads back (measured 10.8 + 7.8
+    // us against 11.9 + 4.2 us at 448x448)
     vp.split_fc2 = gemm_splitk_runs((int)N, c->dim, c->mlp);
   }
-  const int parts = std::max(vp.split_proj, vp.split_fc2);
   vp.off_part = o;
-  if (parts > 1) o = align_up(o + (size_t)parts * N * c->dim * sizeof(float));
+  if (vp.split_fc2 > 1) o = align_up(o + (size_t)vp.split_fc2 * N * c->dim * sizeof(float));
   if (vp.window) {
     vp.off_tokw = o;   o = align_up(o + N * sizeof(int2));
     vp.off_outrow = o; o = align_up(o + (size_t)vp.Pw * sizeof(int32_t));
@@ -563,9 +564,9 @@ qv_status qv_vision_forward(const qv_vision_cfg* c, const qv_vision_w* w, const 
   std::unique_lock<std::mutex> warm_lock;
   if (wc) warm_lock = std::unique_lock<std::mutex>(wc->mu);
   const size_t wb = 2;  // bf16 weights
-  // Split-K (small M): the out-projection and fc2 leave float32 partial sums;
-  // the LayerNorm that follows adds them, the bias and the residual in a
-  // fixed order (after the last block a residual-only pass does it).
+  // Split-K (small M): fc2 leaves float32 partial sums; the next block's
+  // first LayerNorm adds them, the bias and the residual in a fixed order
+  // (after the last block a residual-only pass does it).
   float* part = reinterpret_cast<float*>(base + vp.off_part);
   const size_t part_stride = (size_t)vp.N * c->dim;
   int pending = 0;
@@ -604,13 +605,7 @@ qv_status qv_vision_forward(const qv_vision_cfg* c, const qv_vision_w* w, const 
         QV_LAUNCH(QV_KC_ATTENTION, s, attention_bf16_windows(aw, s));
       else
         QV_LAUNCH(QV_KC_ATTENTION, s, attention_bf16(ab, s));
-      if (vp.split_proj > 1) {
-        QV_LAUNCH(QV_KC_PROJ, s, gemm_bf16_splitk_f32(O, D, b.proj_w, D, M, D, D, vp.split_proj, part, s));
-        pending = vp.split_proj;
-        pending_bias = (const float*)b.proj_b;
-      } else {
-        QV_LAUNCH(QV_KC_PROJ, s, gemm_bf16_resid_f32(O, D, b.proj_w, D, M, D, D, (const float*)b.proj_b, hidden, D, s));
-      }
+      QV_LAUNCH(QV_KC_PROJ, s, gemm_bf16_resid_f32(O, D, b.proj_w, D, M, D, D, (const float*)b.proj_b, hidden, D, s));
     } else {
       float* qkv = reinterpret_cast<float*>(base + vp.off_qkv);
       QV_LAUNCH(QV_KC_QKV, s, gemm_f32_store((const float*)A, D, (const float*)b.qkv_w, D, M, 3 * D, D, (const float*)b.qkv_b, qkv,
