@@ -339,8 +339,8 @@ hipError_t attention_bf16(const AttnArgs& a, hipStream_t s) {
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)kHeadDim);
   const dim3 grid((unsigned)a.total_qtiles * (unsigned)a.heads);
   switch (a.rows_per_wg) {
-    case 128: hipLaunchKernelGGL((k_attn_bf16<4, 2>), grid, dim3(512), 0, s, a, scale_log2); break;
-    case 64: hipLaunchKernelGGL((k_attn_bf16<2, 4>), grid, dim3(512), 0, s, a, scale_log2); break;
+    case 128: QV_KLAUNCH((k_attn_bf16<4, 2>), grid, dim3(512), 0, s, a, scale_log2); break;
+    case 64: QV_KLAUNCH((k_attn_bf16<2, 4>), grid, dim3(512), 0, s, a, scale_log2); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -479,7 +479,7 @@ hipError_t attention_bf16_windows(const AttnArgs& a, hipStream_t s) {
   if (a.n_img == 0) return hipSuccess;
   if (a.P % kWinSlot || !a.out_row) return hipErrorInvalidValue;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)kHeadDim);
-  hipLaunchKernelGGL(k_attn_win, dim3((unsigned)a.n_img * (unsigned)a.heads), dim3(128), 0, s, a, scale_log2);
+  QV_KLAUNCH(k_attn_win, dim3((unsigned)a.n_img * (unsigned)a.heads), dim3(128), 0, s, a, scale_log2);
   return hipGetLastError();
 }
 
@@ -550,7 +550,7 @@ __global__ __launch_bounds__(64) void k_attn_f32(AttnArgs a, float scale) {
 
 hipError_t attention_f32(const AttnArgs& a, hipStream_t s) {
   if (a.total_qtiles == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_attn_f32, dim3((unsigned)a.total_qtiles, (unsigned)a.heads), dim3(64), 0, s, a,
+  QV_KLAUNCH(k_attn_f32, dim3((unsigned)a.total_qtiles, (unsigned)a.heads), dim3(64), 0, s, a,
                      1.0f / sqrtf((float)kHeadDim));
   return hipGetLastError();
 }

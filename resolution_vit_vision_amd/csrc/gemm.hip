@@ -619,7 +619,7 @@ template <int BM, int BN, int WM, int WN, int ST, int KT, int KS = 1, class Epi,
 static hipError_t launch_pipe(const void* A, int lda, const void* B, int ldb, int M, int N, const Epi& epi,
                               RowMap rmap, hipStream_t s) {
   const XcdCut cut = xcd_cut((M + BM - 1) / BM, (N + BN - 1) / BN, BM, BN);
-  hipLaunchKernelGGL((k_gemm_pipe<BM, BN, WM, WN, ST, KT / KS, KS, Epi, RowMap>), dim3(cut.grid), dim3(WM * WN * KS * 64),
+  QV_KLAUNCH((k_gemm_pipe<BM, BN, WM, WN, ST, KT / KS, KS, Epi, RowMap>), dim3(cut.grid), dim3(WM * WN * KS * 64),
                      0, s, reinterpret_cast<const uint16_t*>(A), lda, reinterpret_cast<const uint16_t*>(B), ldb, M, N,
                      cut.xgn, 8, epi, rmap);
   return hipGetLastError();
@@ -630,7 +630,7 @@ static hipError_t launch_ws(const void* A, int lda, const void* B, int ldb, int 
                             RowMap rmap, hipStream_t s, int splits = 1) {
   const XcdCut cut = xcd_cut((M + BM - 1) / BM, (N + BN - 1) / BN, BM, BN);
   // the grid width is a multiple of 8, so workgroup (x, y) still runs on XCD x % 8
-  hipLaunchKernelGGL((k_gemm_ws<BM, BN, WM, WN, ST, KT, NP, Epi, RowMap>), dim3(cut.grid, (unsigned)splits),
+  QV_KLAUNCH((k_gemm_ws<BM, BN, WM, WN, ST, KT, NP, Epi, RowMap>), dim3(cut.grid, (unsigned)splits),
                      dim3((WM * WN + NP) * 64), 0,
                      s, reinterpret_cast<const uint16_t*>(A), lda, reinterpret_cast<const uint16_t*>(B), ldb, M, N,
                      cut.xgn, 8, epi, rmap);
@@ -674,7 +674,7 @@ static hipError_t run_bf16(const void* A, int lda, const void* B, int ldb, int M
   // any other K (the 1176-wide patch embedding): register-staged kernel with K tails
   constexpr int BM = 128, BN = 128;
   const unsigned tiles = (unsigned)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
-  hipLaunchKernelGGL((k_gemm_bf16<BM, BN, 2, 2, Epi, RowMap>), dim3(tiles), dim3(256), 0, s,
+  QV_KLAUNCH((k_gemm_bf16<BM, BN, 2, 2, Epi, RowMap>), dim3(tiles), dim3(256), 0, s,
                      reinterpret_cast<const uint16_t*>(A), lda, reinterpret_cast<const uint16_t*>(B), ldb, M, N, K,
                      epi, rmap);
   return hipGetLastError();
@@ -685,7 +685,7 @@ hipError_t gemm_bf16_store_f32(const void* A, int lda, const void* B, int ldb, i
   if (M <= 0 || N <= 0) return hipSuccess;
   constexpr int BM = 128, BN = 128;
   const unsigned tiles = (unsigned)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
-  hipLaunchKernelGGL((k_gemm_bf16<BM, BN, 2, 2, EpiStoreF32, RowMapIdentity>), dim3(tiles), dim3(256), 0, s,
+  QV_KLAUNCH((k_gemm_bf16<BM, BN, 2, 2, EpiStoreF32, RowMapIdentity>), dim3(tiles), dim3(256), 0, s,
                      reinterpret_cast<const uint16_t*>(A), lda, reinterpret_cast<const uint16_t*>(B), ldb, M, N, K,
                      EpiStoreF32{C, ldc, bias}, RowMapIdentity{});
   return hipGetLastError();
@@ -798,7 +798,7 @@ static hipError_t run_f32(const float* A, int lda, const float* B, int ldb, int 
                           hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
   const unsigned tiles = (unsigned)(((M + 63) / 64) * ((N + 63) / 64));
-  hipLaunchKernelGGL(k_gemm_f32<Epi>, dim3(tiles), dim3(256), 0, s, A, lda, B, ldb, M, N, K, e);
+  QV_KLAUNCH(k_gemm_f32<Epi>, dim3(tiles), dim3(256), 0, s, A, lda, B, ldb, M, N, K, e);
   return hipGetLastError();
 }
 
@@ -846,7 +846,7 @@ __global__ __launch_bounds__(256) void k_rope_scatter_f32(const float* __restric
 hipError_t rope_scatter_f32(const float* qkv, int M, const float*, const QkvOut& o, hipStream_t s) {
   const int64_t n = (int64_t)M * 2 * o.dim;
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_rope_scatter_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, qkv, M, o);
+  QV_KLAUNCH(k_rope_scatter_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, qkv, M, o);
   return hipGetLastError();
 }
 

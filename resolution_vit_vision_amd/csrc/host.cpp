@@ -39,6 +39,11 @@ qv_status fail(qv_status st, const char* fmt, ...) {
   } while (0)
 
 // ------------------------------------------------- launch timing (diagnostic)
+}  // namespace
+namespace qv {
+thread_local LaunchTiming* g_launch_timing = nullptr;
+}  // namespace qv
+namespace {
 struct Timing {
   std::mutex mu;
   int cls = -1;
@@ -65,12 +70,36 @@ std::pair<hipEvent_t, hipEvent_t>* timing_slot(int cls) {
   return &t.pool[t.used++];
 }
 
+// Gives back the last slot when the timed call launched no kernel.
+void timing_unslot() {
+  Timing& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  if (t.used) --t.used;
+}
+
+// Points the kernel launches of one call at an event pair for its lifetime.
+struct TimingScope {
+  LaunchTiming lt;
+  explicit TimingScope(std::pair<hipEvent_t, hipEvent_t>* s) : lt{s->first, s->second, false} {
+    g_launch_timing = &lt;
+  }
+  ~TimingScope() { g_launch_timing = nullptr; }
+};
+
 #define QV_LAUNCH(cls, stream, call)                                       \
   do {                                                                     \
     auto* slot_ = timing_slot(cls);                                        \
-    if (slot_) QV_HIP(hipEventRecord(slot_->first, stream));               \
-    QV_HIP(call);                                                          \
-    if (slot_) QV_HIP(hipEventRecord(slot_->second, stream));              \
+    if (slot_) {                                                           \
+      bool launched_ = false;                                              \
+      {                                                                    \
+        TimingScope ts_(slot_);                                            \
+        QV_HIP(call);                                                      \
+        launched_ = ts_.lt.started;                                        \
+      }                                                                    \
+      if (!launched_) timing_unslot();                                     \
+    } else {                                                               \
+      QV_HIP(call);                                                        \
+    }                                                                      \
   } while (0)
 
 // Weight warm-up: a side stream (default priority) on which small read-only

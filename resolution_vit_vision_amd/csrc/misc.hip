@@ -76,7 +76,7 @@ hipError_t launch_patchify(const float* pixels, const PatchChunk& c, int patch, 
   const int64_t threads = rows_in_chunk_max * (m.width / 8);
   if (threads == 0) return hipSuccess;
   dim3 grid((unsigned)((threads + 255) / 256), (unsigned)c.count);
-  hipLaunchKernelGGL(k_patchify, grid, dim3(256), 0, s, pixels, c, patch, temporal, out, bf16 ? 1 : 0, ld, m);
+  QV_KLAUNCH(k_patchify, grid, dim3(256), 0, s, pixels, c, patch, temporal, out, bf16 ? 1 : 0, ld, m);
   return hipGetLastError();
 }
 
@@ -110,7 +110,7 @@ hipError_t launch_fold_weight(const void* w, int dim, int channels, int patch, i
                               int ld_out, bool bf16, hipStream_t s) {
   const int64_t total = (int64_t)dim * ld_out;
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_fold_weight, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, w, dim, channels, patch,
+  QV_KLAUNCH(k_fold_weight, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, w, dim, channels, patch,
                      temporal, ld_in, out, ld_out, bf16 ? 1 : 0);
   return hipGetLastError();
 }
@@ -137,7 +137,7 @@ hipError_t launch_setup_tokens(const DescChunk& c, int2* tokinfo, hipStream_t s)
   for (int i = 0; i < c.count; ++i) nmax = c.d[i].n > nmax ? c.d[i].n : nmax;
   if (nmax == 0) return hipSuccess;
   dim3 grid((unsigned)((nmax + 255) / 256), (unsigned)c.count);
-  hipLaunchKernelGGL(k_setup_tokens, grid, dim3(256), 0, s, c, tokinfo);
+  QV_KLAUNCH(k_setup_tokens, grid, dim3(256), 0, s, c, tokinfo);
   return hipGetLastError();
 }
 
@@ -176,7 +176,7 @@ hipError_t launch_setup_windows(const DescChunk& c, int window, int slot, int2* 
   for (int i = 0; i < c.count; ++i) nmax = c.d[i].n > nmax ? c.d[i].n : nmax;
   if (nmax == 0) return hipSuccess;
   dim3 grid((unsigned)((nmax + 255) / 256), (unsigned)c.count);
-  hipLaunchKernelGGL(k_setup_windows, grid, dim3(256), 0, s, c, window, slot, tokinfo_w, out_row);
+  QV_KLAUNCH(k_setup_windows, grid, dim3(256), 0, s, c, window, slot, tokinfo_w, out_row);
   return hipGetLastError();
 }
 
@@ -197,7 +197,7 @@ hipError_t launch_setup_plan(const PlanEntry* host_plan_chunk, int count, int fi
   c.count = count;
   c.first = first;
   for (int i = 0; i < count; ++i) c.e[i] = host_plan_chunk[i];
-  hipLaunchKernelGGL(k_setup_plan, dim3(1), dim3(kPlanChunk), 0, s, c, plan);
+  QV_KLAUNCH(k_setup_plan, dim3(1), dim3(kPlanChunk), 0, s, c, plan);
   return hipGetLastError();
 }
 
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(256) void k_rope_table(float2* __restrict__ tab, in
 
 hipError_t launch_rope_table(float2* tab, int positions, float theta, hipStream_t s) {
   const int n = positions * kRopeFreqs;
-  hipLaunchKernelGGL(k_rope_table, dim3((n + 255) / 256), dim3(256), 0, s, tab, positions, (double)theta);
+  QV_KLAUNCH(k_rope_table, dim3((n + 255) / 256), dim3(256), 0, s, tab, positions, (double)theta);
   return hipGetLastError();
 }
 
@@ -227,7 +227,7 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
   if (n16 == 0) return hipSuccess;
   size_t blocks = (n16 + 255) / 256;
   if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(k_zero, dim3((unsigned)blocks), dim3(256), 0, s, reinterpret_cast<uint4*>(p), n16);
+  QV_KLAUNCH(k_zero, dim3((unsigned)blocks), dim3(256), 0, s, reinterpret_cast<uint4*>(p), n16);
   return hipGetLastError();
 }
 
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(64) void k_warm(const uint4* __restrict__ src, size
 
 hipError_t launch_warm(const void* src, size_t bytes, hipStream_t s) {
   if (!src || bytes < 16) return hipSuccess;
-  hipLaunchKernelGGL(k_warm, dim3(256), dim3(64), 0, s, reinterpret_cast<const uint4*>(src), bytes / 16);
+  QV_KLAUNCH(k_warm, dim3(256), dim3(64), 0, s, reinterpret_cast<const uint4*>(src), bytes / 16);
   return hipGetLastError();
 }
 
@@ -405,9 +405,9 @@ hipError_t launch_layernorm_acc(float* x, const float* parts, size_t part_stride
   if (dim != 1280) return hipErrorInvalidValue;
   dim3 grid((unsigned)((rows + 3) / 4));
   switch (splits) {
-    case 2: hipLaunchKernelGGL((k_layernorm_acc<5, 2>), grid, dim3(256), 0, s, x, parts, part_stride, pb, g, b, y,
+    case 2: QV_KLAUNCH((k_layernorm_acc<5, 2>), grid, dim3(256), 0, s, x, parts, part_stride, pb, g, b, y,
                                bf16 ? 1 : 0, rows, eps); break;
-    case 4: hipLaunchKernelGGL((k_layernorm_acc<5, 4>), grid, dim3(256), 0, s, x, parts, part_stride, pb, g, b, y,
+    case 4: QV_KLAUNCH((k_layernorm_acc<5, 4>), grid, dim3(256), 0, s, x, parts, part_stride, pb, g, b, y,
                                bf16 ? 1 : 0, rows, eps); break;
     default: return hipErrorInvalidValue;
   }
@@ -419,10 +419,10 @@ hipError_t launch_layernorm(const float* x, const float* g, const float* b, void
   dim3 grid((unsigned)((rows + 3) / 4));
   const int nv = dim / 256;
   switch (nv) {
-    case 4: hipLaunchKernelGGL(k_layernorm<4>, grid, dim3(256), 0, s, x, g, b, y, bf16 ? 1 : 0, rows, eps); break;
-    case 5: hipLaunchKernelGGL(k_layernorm<5>, grid, dim3(256), 0, s, x, g, b, y, bf16 ? 1 : 0, rows, eps); break;
-    case 6: hipLaunchKernelGGL(k_layernorm<6>, grid, dim3(256), 0, s, x, g, b, y, bf16 ? 1 : 0, rows, eps); break;
-    case 8: hipLaunchKernelGGL(k_layernorm<8>, grid, dim3(256), 0, s, x, g, b, y, bf16 ? 1 : 0, rows, eps); break;
+    case 4: QV_KLAUNCH(k_layernorm<4>, grid, dim3(256), 0, s, x, g, b, y, bf16 ? 1 : 0, rows, eps); break;
+    case 5: QV_KLAUNCH(k_layernorm<5>, grid, dim3(256), 0, s, x, g, b, y, bf16 ? 1 : 0, rows, eps); break;
+    case 6: QV_KLAUNCH(k_layernorm<6>, grid, dim3(256), 0, s, x, g, b, y, bf16 ? 1 : 0, rows, eps); break;
+    case 8: QV_KLAUNCH(k_layernorm<8>, grid, dim3(256), 0, s, x, g, b, y, bf16 ? 1 : 0, rows, eps); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -2,10 +2,36 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace qv {
+
+// Launch timing (diagnostics): while a launch class is being timed, the host
+// points g_launch_timing at an event pair and every kernel launch of that
+// class goes through hipExtLaunchKernelGGL, whose events take the dispatch's
+// own begin / end timestamps (the first launch records `start`, every launch
+// re-records `stop`).  Otherwise a plain launch.
+struct LaunchTiming {
+  hipEvent_t start;
+  hipEvent_t stop;
+  bool started;
+};
+extern thread_local LaunchTiming* g_launch_timing;
+
+#define QV_KLAUNCH(kernel, grid, block, shm, stream, ...)                                                   \
+  do {                                                                                                      \
+    ::qv::LaunchTiming* t_ = ::qv::g_launch_timing;                                                         \
+    if (t_) {                                                                                               \
+      hipExtLaunchKernelGGL(kernel, grid, block, shm, stream, t_->started ? nullptr : t_->start, t_->stop, 0, \
+                            __VA_ARGS__);                                                                   \
+      t_->started = true;                                                                                   \
+    } else {                                                                                                \
+      hipLaunchKernelGGL(kernel, grid, block, shm, stream, __VA_ARGS__);                                    \
+    }                                                                                                       \
+  } while (0)
+
 
 constexpr int kHeadDim = 80;       // attention kernels are written for 80-wide heads
 constexpr int kRopeFreqs = kHeadDim / 4;
