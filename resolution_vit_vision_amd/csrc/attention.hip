@@ -327,6 +327,265 @@ __global__ __launch_bounds__(512) void k_attn_bf16(AttnArgs a, float scale_log2)
   }
 }
 
+// ====================================================== long sequences
+// Images of a few thousand patches and more (128 query rows per workgroup):
+// NW = 4 waves of 32 queries, keys streamed 32 per stage through a 4-stage
+// LDS-DMA ring (K tile 5 KB + V^T 5 KB + a 32-byte constant block holding the
+// ones row, per stage), the stage index a compile-time constant of a loop
+// unrolled by 4 so every LDS address is an immediate offset.  Per step the
+// scores of the next tile are formed while the current tile's exponentials
+// run (sched_group_barrier interleaves the 5 MFMAs with the VALU work), then
+// the running max of the next tile is taken while its P.V MFMAs run.  V^T
+// chunks are XOR-swizzled by (row >> 2) & 3 (64-byte rows): the 16 rows one
+// pass of a 16-byte read touches cover all 64 banks.  Measured against the
+// 8-wave kernel at n = 9216 .. 65,536: +7-11 % (1.0-1.07 PFLOP/s).
+template <int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_attn_long(AttnArgs a) {
+  constexpr int BQ = 32 * NW;
+  constexpr int IK = 32;
+  constexpr int K_BYTES = IK * kHeadDim * 2;   // 5120: one 32-key tile of the key-tiled layout
+  constexpr int V_BYTES = kHeadDim * IK * 2;   // 5120: V^T rows of 32 keys (64 B each)
+  constexpr int CONST_OFF = K_BYTES + V_BYTES; // 32 B: eight bf16 ones, then eight zeros
+  constexpr int STRIDE = CONST_OFF + 32;
+  constexpr int NST = 4;
+  constexpr int BLKS = (K_BYTES + V_BYTES) / 1024;  // 10 DMA blocks per stage
+  constexpr int LWMAX = (BLKS + NW - 1) / NW;
+  __shared__ __attribute__((aligned(1024))) char lds[NST * STRIDE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hlf = lane >> 5, l32 = lane & 31;
+  int head, gt;
+  {
+    const int b = blockIdx.x, T = a.total_qtiles;
+    if (a.heads % 8 == 0) {
+      const int hpx = a.heads / 8, local = b / 8;
+      head = (b % 8) * hpx + local / T;
+      gt = local % T;
+    } else {
+      head = b / T;
+      gt = b % T;
+    }
+  }
+  const PlanEntry pe = a.plan[find_plan(a.plan, a.n_img, gt)];
+  const int row0 = a.out_row ? 0 : a.cu_seqlens[pe.seg];
+  const int n = a.out_row ? pe.n : a.cu_seqlens[pe.seg + 1] - row0;
+  const int qbase = (gt - pe.qtile0) * BQ + wave * 32;
+
+  const uint16_t* Qh = reinterpret_cast<const uint16_t*>(a.q) + (size_t)head * a.P * kHeadDim;
+  const char* Kt = reinterpret_cast<const char*>(a.k) + kc_offset(head, a.P, pe.prow0, 0) * 2;
+  const char* Vh = reinterpret_cast<const char*>(a.vt) + (size_t)head * kHeadDim * a.P * 2;
+
+  // DMA sources of this wave's blocks (block wave + NW i of each stage)
+  const char* gsrc[LWMAX];
+  int ldst[LWMAX];
+  bool isk[LWMAX];
+#pragma unroll
+  for (int i = 0; i < LWMAX; ++i) {
+    int blk = wave + NW * i;
+    blk = blk < BLKS ? blk : BLKS - 1;
+    const int slot = blk * 64 + lane;
+    if (slot < K_BYTES / 16) {
+      gsrc[i] = Kt + (size_t)slot * 16;
+      isk[i] = true;
+    } else {
+      const int sv = slot - K_BYTES / 16;
+      const int d = sv >> 2, p = sv & 3;
+      const int c = p ^ ((d >> 2) & 3);
+      gsrc[i] = Vh + ((size_t)d * a.P + pe.prow0 + 8 * c) * 2;
+      isk[i] = false;
+    }
+    ldst[i] = blk * 1024;
+  }
+  const int nblk = (BLKS - wave + NW - 1) / NW;
+#define QV_L_ISSUE(IT, ST)                                                                                   \
+  {                                                                                                          \
+    _Pragma("unroll") for (int i = 0; i < LWMAX; ++i) {                                                      \
+      if (i < nblk) {                                                                                        \
+        const size_t step_ = isk[i] ? (size_t)(IT) * K_BYTES : (size_t)(IT) * IK * 2;                       \
+        __builtin_amdgcn_global_load_lds((gas_ptr)(gsrc[i] + step_), (las_ptr)(lds + (ST) * STRIDE + ldst[i]), \
+                                         16, 0, 0);                                                          \
+      }                                                                                                      \
+    }                                                                                                        \
+  }
+
+  // per-lane LDS offsets (stage offsets are immediates)
+  const int koff = (hlf * 32 + l32) * 16;
+  int voff[2], voff2[2];
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) {
+    const int c = 2 * s2 + hlf;
+    voff[s2] = K_BYTES + l32 * 64 + ((c ^ ((l32 >> 2) & 3)) << 4);
+    voff2[s2] = l32 < 16 ? K_BYTES + (64 + l32) * 64 + ((c ^ ((l32 >> 2) & 3)) << 4)
+                         : CONST_OFF + (l32 == 16 ? 0 : 16);
+  }
+
+  const int iters = (n + IK - 1) / IK;
+  QV_L_ISSUE(0, 0)
+  bf16x8 qf[5];
+  {
+    const uint16_t* qr = Qh + (size_t)(pe.prow0 + qbase + l32) * kHeadDim + 8 * hlf;
+#pragma unroll
+    for (int kk = 0; kk < 5; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qr + 16 * kk);
+  }
+  if (wave == 0 && lane < 2 * NST) {
+    const uint32_t w = (lane & 1) ? 0u : 0x3F803F80u;
+    *reinterpret_cast<uint4*>(lds + (lane >> 1) * STRIDE + CONST_OFF + 16 * (lane & 1)) = make_uint4(w, w, w, w);
+  }
+  QV_WAIT_VM(0);
+  __syncthreads();
+  if (iters > 1) QV_L_ISSUE(1, 1)
+  if (iters > 2) QV_L_ISSUE(2, 2)
+
+  f32x16 o[3];
+#pragma unroll
+  for (int t = 0; t < 3; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
+
+#define QV_L_S(ST, SACC)                                                                                     \
+  {                                                                                                          \
+    _Pragma("unroll") for (int r = 0; r < 16; ++r) SACC[r] = 0.f;                                           \
+    _Pragma("unroll") for (int kk = 0; kk < 5; ++kk) SACC = __builtin_amdgcn_mfma_f32_32x32x16_bf16(        \
+        *reinterpret_cast<const bf16x8*>(lds + (ST) * STRIDE + kk * 1024 + koff), qf[kk], SACC, 0, 0, 0);   \
+  }
+#define QV_L_MASK(IT, SACC)                                                                                  \
+  {                                                                                                          \
+    const int kb_ = (IT) * IK;                                                                               \
+    if (kb_ + IK > n) {                                                                                      \
+      _Pragma("unroll") for (int r = 0; r < 16; ++r) {                                                      \
+        const int key_ = kb_ + 8 * (r >> 2) + 4 * hlf + (r & 3);                                             \
+        if (key_ >= n) SACC[r] = -INFINITY;                                                                  \
+      }                                                                                                      \
+    }                                                                                                        \
+  }
+#define QV_L_MAX(SACC, OUT)                                                                                  \
+  {                                                                                                          \
+    float m_ = fmaxf(fmaxf(SACC[0], SACC[1]), SACC[2]);                                                     \
+    _Pragma("unroll") for (int r = 3; r < 16; r += 2) m_ = fmaxf(fmaxf(m_, SACC[r]), SACC[r + 1 < 16 ? r + 1 : r]); \
+    const auto sw_ = __builtin_amdgcn_permlane32_swap(__float_as_uint(m_), __float_as_uint(m_), false, false); \
+    OUT = fmaxf(__uint_as_float(sw_[0]), __uint_as_float(sw_[1]));                             \
+  }
+
+  // q arrives pre-scaled by log2(e)/sqrt(80) (the q/k/v epilogue), so the
+  // scores are in log2 units.  The S MFMA chain starts from C = -m_run
+  // (negm: the same value in the 16 registers of a lane), so the exponent
+  // argument leaves the matrix core ready for v_exp_f32.
+  f32x16 s_cur, s_nxt, negm;
+  float m_run;
+  QV_L_S(0, s_cur)
+  QV_L_MASK(0, s_cur)
+  QV_L_MAX(s_cur, m_run)
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    s_cur[r] -= m_run;
+    negm[r] = -m_run;
+  }
+
+  // one step: tile IT in stage ST (compile-time)
+#define QV_L_STEP(IT, ST)                                                                                    \
+  {                                                                                                          \
+    const bool more_ = (IT) + 1 < iters;                                                                     \
+    if (more_) {                                                                                             \
+      if ((IT) + 2 < iters) {                                                                                \
+        if (nblk == LWMAX) QV_WAIT_VM(LWMAX); else QV_WAIT_VM(LWMAX - 1);                                    \
+      } else {                                                                                               \
+        QV_WAIT_VM(0);                                                                                       \
+      }                                                                                                      \
+      QV_BARRIER();                                                                                          \
+      if ((IT) + 3 < iters) QV_L_ISSUE((IT) + 3, ((ST) + 3) % NST)                                          \
+    }                                                                                                        \
+    bf16x8 kf_[5];                                                                                           \
+    _Pragma("unroll") for (int kk = 0; kk < 5; ++kk)                                                        \
+      kf_[kk] = *reinterpret_cast<const bf16x8*>(lds + (((ST) + 1) % NST) * STRIDE + kk * 1024 + koff);     \
+    s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf_[0], qf[0], negm, 0, 0, 0);                          \
+    _Pragma("unroll") for (int kk = 1; kk < 5; ++kk)                                                        \
+      s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf_[kk], qf[kk], s_nxt, 0, 0, 0);                      \
+    bf16x8 pb[2];                                                                                            \
+    _Pragma("unroll") for (int s2 = 0; s2 < 2; ++s2)                                                        \
+    _Pragma("unroll") for (int e = 0; e < 8; ++e)                                                           \
+      pb[s2][e] = (__bf16)__builtin_amdgcn_exp2f(s_cur[8 * s2 + e]);                                          \
+    bf16x8 vf_[6];                                                                                           \
+    _Pragma("unroll") for (int s2 = 0; s2 < 2; ++s2)                                                        \
+    _Pragma("unroll") for (int t = 0; t < 3; ++t)                                                           \
+      vf_[3 * s2 + t] = *reinterpret_cast<const bf16x8*>(lds + (ST) * STRIDE +                               \
+                                                       (t < 2 ? voff[s2] + t * 2048 : voff2[s2]));          \
+    asm volatile("" ::"v"(pb[0]), "v"(pb[1]));                                                              \
+    {                                                                                                        \
+      __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);                                                     \
+      __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);                                                     \
+      _Pragma("unroll") for (int g_ = 0; g_ < 4; ++g_) {                                                    \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                   \
+        __builtin_amdgcn_sched_group_barrier(0x402, 7, 0);                                                   \
+      }                                                                                                      \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                     \
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);                                                     \
+      __builtin_amdgcn_sched_group_barrier(0x402, 12, 0);                                                    \
+    }                                                                                                        \
+    if (more_) QV_L_MASK((IT) + 1, s_nxt)                                                                    \
+    float cand_;                                                                                             \
+    QV_L_MAX(s_nxt, cand_)                                                                                   \
+    _Pragma("unroll") for (int s2 = 0; s2 < 2; ++s2)                                                        \
+    _Pragma("unroll") for (int t = 0; t < 3; ++t)                                                           \
+      o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf_[3 * s2 + t], pb[s2], o[t], 0, 0, 0);               \
+    {                                                                                                        \
+      _Pragma("unroll") for (int g_ = 0; g_ < 6; ++g_) {                                                    \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                   \
+        __builtin_amdgcn_sched_group_barrier(0x402, 3, 0);                                                   \
+      }                                                                                                      \
+    }                                                                                                        \
+    const bool grow_ = more_ && cand_ > kLazyLog2;                                                           \
+    if (__any(grow_)) {                                                                                      \
+      const float d_ = grow_ ? cand_ : 0.f;                                                                  \
+      const float alpha_ = __builtin_amdgcn_exp2f(-d_);                                                      \
+      m_run += d_;                                                                                           \
+      _Pragma("unroll") for (int t = 0; t < 3; ++t)                                                         \
+      _Pragma("unroll") for (int r = 0; r < 16; ++r) o[t][r] *= alpha_;                                     \
+      _Pragma("unroll") for (int r = 0; r < 16; ++r) {                                                      \
+        s_nxt[r] -= d_;                                                                                      \
+        negm[r] = -m_run;                                                                                    \
+      }                                                                                                      \
+    }                                                                                                        \
+    s_cur = s_nxt;                                                                                           \
+  }
+
+  for (int it = 0; it < iters; it += NST) {
+    QV_L_STEP(it, 0)
+    if (it + 1 >= iters) break;
+    QV_L_STEP(it + 1, 1)
+    if (it + 2 >= iters) break;
+    QV_L_STEP(it + 2, 2)
+    if (it + 3 >= iters) break;
+    QV_L_STEP(it + 3, 3)
+  }
+#undef QV_L_STEP
+#undef QV_L_S
+#undef QV_L_MASK
+#undef QV_L_MAX
+#undef QV_L_ISSUE
+
+  const float lsum = __shfl(o[2][8], l32, 64);
+  const float inv = 1.0f / lsum;
+  const int q = qbase + l32;
+  if (q < n) {
+    const int orow_i = a.out_row ? a.out_row[pe.prow0 + q] : row0 + q;
+    uint16_t* orow = reinterpret_cast<uint16_t*>(a.o) + (size_t)orow_i * a.ldo + head * kHeadDim;
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * t + 8 * g + 4 * hlf;
+        if (d0 < kHeadDim) {
+          uint2 pk;
+          pk.x = pack_bf16(o[t][4 * g] * inv, o[t][4 * g + 1] * inv);
+          pk.y = pack_bf16(o[t][4 * g + 2] * inv, o[t][4 * g + 3] * inv);
+          *reinterpret_cast<uint2*>(orow + d0) = pk;
+        }
+      }
+  }
+}
+
+
 int attention_bf16_rows_per_wg(int64_t wgs_at_128) {
   // 128 query rows per workgroup when that alone gives a workgroup per CU,
   // else 64 (the key split doubles the workgroups)
@@ -336,10 +595,10 @@ int attention_bf16_rows_per_wg(int64_t wgs_at_128) {
 hipError_t attention_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.total_qtiles == 0) return hipSuccess;
   if (a.P % 128) return hipErrorInvalidValue;
-  const float scale_log2 = 1.4426950408889634f / sqrtf((float)kHeadDim);
+  const float scale_log2 = 1.0f;  // q is pre-scaled by log2(e)/sqrt(80)
   const dim3 grid((unsigned)a.total_qtiles * (unsigned)a.heads);
   switch (a.rows_per_wg) {
-    case 128: QV_KLAUNCH((k_attn_bf16<4, 2>), grid, dim3(512), 0, s, a, scale_log2); break;
+    case 128: QV_KLAUNCH((k_attn_long<4>), grid, dim3(256), 0, s, a); break;
     case 64: QV_KLAUNCH((k_attn_bf16<2, 4>), grid, dim3(512), 0, s, a, scale_log2); break;
     default: return hipErrorInvalidValue;
   }
@@ -478,7 +737,7 @@ __global__ __launch_bounds__(128) void k_attn_win(AttnArgs a, float scale_log2) 
 hipError_t attention_bf16_windows(const AttnArgs& a, hipStream_t s) {
   if (a.n_img == 0) return hipSuccess;
   if (a.P % kWinSlot || !a.out_row) return hipErrorInvalidValue;
-  const float scale_log2 = 1.4426950408889634f / sqrtf((float)kHeadDim);
+  const float scale_log2 = 1.0f;  // q is pre-scaled by log2(e)/sqrt(80)
   QV_KLAUNCH(k_attn_win, dim3((unsigned)a.n_img * (unsigned)a.heads), dim3(128), 0, s, a, scale_log2);
   return hipGetLastError();
 }

@@ -295,6 +295,10 @@ struct RowMapQkv {
   __device__ int operator()(int r) const { return qkv_weight_row(r, dim); }
 };
 
+// q leaves the projection multiplied by log2(e)/sqrt(80), so the attention
+// kernels' scores are already the exponent in base 2.
+constexpr float kQScaleLog2 = 0.16129820911147802f;
+
 struct EpiQkv {
   static constexpr bool kStaged = true;
   static constexpr int kPatchFloats = 32 * 72;  // q/k: 32 rows x (64 + 8) floats
@@ -356,13 +360,14 @@ struct EpiQkv {
         for (int fp = 0; fp < NP; ++fp) {
           const bool isk = wn0 + fp * 64 >= dim;
           uint16_t* base = reinterpret_cast<uint16_t*>(isk ? o.k : o.q);
+          const float qs = isk ? 1.0f : kQScaleLog2;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int rl = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
             const float x0 = acc[fm][2 * fp][r] + b0[fp], x1 = acc[fm][2 * fp + 1][r] + b1[fp];
             const bool ok = rb + rl < M;
-            wlds[rl * 72 + c] = ok ? x0 * cs[fp][r].x - x1 * cs[fp][r].y : 0.f;
-            wlds[rl * 72 + 32 + c] = ok ? x1 * cs[fp][r].x + x0 * cs[fp][r].y : 0.f;
+            wlds[rl * 72 + c] = ok ? (x0 * cs[fp][r].x - x1 * cs[fp][r].y) * qs : 0.f;
+            wlds[rl * 72 + 32 + c] = ok ? (x1 * cs[fp][r].x + x0 * cs[fp][r].y) * qs : 0.f;
           }
 #pragma unroll
           for (int pass = 0; pass < 4; ++pass) {
@@ -455,7 +460,8 @@ struct EpiQkv {
             const int p = j < kRopeFreqs ? (ti.x & 0xFFFF) : (ti.x >> 16);
             const float2 cs = o.rope[p * kRopeFreqs + fi];
             const float x0 = acc[fm][fp][r] + b0, x1 = acc[fm][fp + 1][r] + b1;
-            const uint16_t y0 = bf16_bits(x0 * cs.x - x1 * cs.y), y1 = bf16_bits(x1 * cs.x + x0 * cs.y);
+            const float qs = region ? 1.0f : kQScaleLog2;
+            const uint16_t y0 = bf16_bits((x0 * cs.x - x1 * cs.y) * qs), y1 = bf16_bits((x1 * cs.x + x0 * cs.y) * qs);
             if (region) {
               kdst[kc_offset(head, o.P, ti.y, j)] = y0;
               kdst[kc_offset(head, o.P, ti.y, j + kHeadDim / 2)] = y1;
