@@ -339,6 +339,11 @@ __global__ __launch_bounds__(512) void k_attn_bf16(AttnArgs a, float scale_log2)
 // chunks are XOR-swizzled by (row >> 2) & 3 (64-byte rows): the 16 rows one
 // pass of a 16-byte read touches cover all 64 banks.  Measured against the
 // 8-wave kernel at n = 9216 .. 65,536: +7-11 % (1.0-1.07 PFLOP/s).
+// The occupancy request of 4 waves per SIMD is not met (168 VGPRs leave 3),
+// but the schedule the compiler builds under it measured 8-10 % faster than
+// with no request or a request of 3; the unmet-target warning is silenced.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Wpass-failed"
 template <int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_attn_long(AttnArgs a) {
   constexpr int BQ = 32 * NW;
@@ -585,6 +590,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
   }
 }
 
+
+#pragma clang diagnostic pop
 
 int attention_bf16_rows_per_wg(int64_t wgs_at_128) {
   // 128 query rows per workgroup when that alone gives a workgroup per CU,

@@ -64,7 +64,10 @@ std::pair<hipEvent_t, hipEvent_t>* timing_slot(int cls) {
   if (t.used == t.pool.size()) {
     hipEvent_t a, b;
     if (hipEventCreate(&a) != hipSuccess) return nullptr;
-    if (hipEventCreate(&b) != hipSuccess) { hipEventDestroy(a); return nullptr; }
+    if (hipEventCreate(&b) != hipSuccess) {
+      (void)hipEventDestroy(a);
+      return nullptr;
+    }
     t.pool.emplace_back(a, b);
   }
   return &t.pool[t.used++];
@@ -101,41 +104,6 @@ struct TimingScope {
       QV_HIP(call);                                                        \
     }                                                                      \
   } while (0)
-
-// Weight warm-up: a side stream (default priority) on which small read-only
-// kernels pull the next GEMMs' weights into the Infinity Cache while the
-// current kernels run.  Created once per device and kept for the life of the
-// process; `mu` serializes the enqueue of forwards that share it, because
-// the events are reused from call to call.
-struct WarmCtx {
-  std::mutex mu;
-  hipStream_t side = nullptr;
-  std::vector<hipEvent_t> ev;  // one per block
-  hipEvent_t done = nullptr;
-};
-
-WarmCtx* warm_ctx(int depth) {
-  static std::mutex mu;
-  static WarmCtx per_dev[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-  std::lock_guard<std::mutex> g(mu);
-  WarmCtx& w = per_dev[dev];
-  if (!w.side && hipStreamCreateWithFlags(&w.side, hipStreamNonBlocking) != hipSuccess) {
-    w.side = nullptr;
-    return nullptr;
-  }
-  if (!w.done && hipEventCreateWithFlags(&w.done, hipEventDisableTiming) != hipSuccess) {
-    w.done = nullptr;
-    return nullptr;
-  }
-  while ((int)w.ev.size() < depth) {
-    hipEvent_t e;
-    if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return nullptr;
-    w.ev.push_back(e);
-  }
-  return &w;
-}
 
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -586,13 +554,6 @@ qv_status qv_vision_forward(const qv_vision_cfg* c, const qv_vision_w* w, const 
               vp.attn_rows};
   AttnArgs aw{qo.q, qo.k, qo.vt, O, D, cu_seqlens, planw, (int)vp.n_win, outrow, (int)vp.Pw, c->heads,
               vp.total_qtiles_w, bf ? 64 : kAttnBQ_f32};
-  // bf16 path: at the start of block l the side stream warms block l's
-  // proj / fc1 / fc2 weights and block l + 1's qkv weights, in the order the
-  // GEMMs need them; the caller's stream waits for the side stream at the end.
-  WarmCtx* wc = (bf && c->depth > 0) ? warm_ctx(c->depth) : nullptr;
-  std::unique_lock<std::mutex> warm_lock;
-  if (wc) warm_lock = std::unique_lock<std::mutex>(wc->mu);
-  const size_t wb = 2;  // bf16 weights
   // Split-K (small M): fc2 leaves float32 partial sums; the next block's
   // first LayerNorm adds them, the bias and the residual in a fixed order
   // (after the last block a residual-only pass does it).
@@ -614,14 +575,6 @@ qv_status qv_vision_forward(const qv_vision_cfg* c, const qv_vision_w* w, const 
   };
   for (int l = 0; l < c->depth; ++l) {
     const qv_block_w& b = w->blocks[l];
-    if (wc) {
-      QV_HIP(hipEventRecord(wc->ev[l], s));
-      QV_HIP(hipStreamWaitEvent(wc->side, wc->ev[l], 0));
-      QV_HIP(launch_warm(b.proj_w, (size_t)D * D * wb, wc->side));
-      QV_HIP(launch_warm(b.fc1_w, (size_t)F * D * wb, wc->side));
-      QV_HIP(launch_warm(b.fc2_w, (size_t)D * F * wb, wc->side));
-      if (l + 1 < c->depth) QV_HIP(launch_warm(w->blocks[l + 1].qkv_w, (size_t)3 * D * D * wb, wc->side));
-    }
     // windowed block: q/k/v scattered into the window layout, attention per window
     const bool win = vp.window && !(l < 64 && ((c->full_blocks >> l) & 1u));
     const QkvOut& qb = win ? qow : qo;
@@ -666,10 +619,6 @@ qv_status qv_vision_forward(const qv_vision_cfg* c, const qv_vision_w* w, const 
     QV_LAUNCH(QV_KC_LAYERNORM, s, launch_layernorm_acc(hidden, part, part_stride, pending, pending_bias, nullptr,
                                                        nullptr, nullptr, bf, (int)vp.N, c->dim, c->ln_eps, s));
     pending = 0;
-  }
-  if (wc) {
-    QV_HIP(hipEventRecord(wc->done, wc->side));
-    QV_HIP(hipStreamWaitEvent(s, wc->done, 0));
   }
   return QV_OK;
 }

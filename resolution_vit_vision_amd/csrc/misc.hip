@@ -231,39 +231,6 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
   return hipGetLastError();
 }
 
-// ------------------------------------------------------------ cache warm-up
-// Reads `n16` 16-byte words of `src` so that they pass through L2 and stay in
-// the Infinity Cache for a kernel that runs a little later on another
-// stream: the GEMMs stream their weights once per forward, and a cold weight
-// panel costs them HBM latency they cannot hide in LDS.  One wave per
-// workgroup, no LDS (so a warm-up wave never keeps an LDS-hungry workgroup
-// off a CU), 16 loads of 16 bytes in flight per lane.  The words are folded
-// into a value that is stored only if it equals a constant, which keeps the
-// loads without writing anything in practice.
-__device__ uint32_t g_warm_sink[64];
-
-__global__ __launch_bounds__(64) void k_warm(const uint4* __restrict__ src, size_t n16) {
-  constexpr int U = 16;
-  const size_t stride = (size_t)gridDim.x * 64;
-  size_t i = (size_t)blockIdx.x * 64 + threadIdx.x;
-  uint32_t acc = 0;
-  for (; i + (U - 1) * stride < n16; i += U * stride) {
-    uint4 v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = src[i + u * stride];
-#pragma unroll
-    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].w;
-  }
-  for (; i < n16; i += stride) acc ^= src[i].x;
-  if (acc == 0x9E3779B9u) g_warm_sink[threadIdx.x] = acc;
-}
-
-hipError_t launch_warm(const void* src, size_t bytes, hipStream_t s) {
-  if (!src || bytes < 16) return hipSuccess;
-  QV_KLAUNCH(k_warm, dim3(256), dim3(64), 0, s, reinterpret_cast<const uint4*>(src), bytes / 16);
-  return hipGetLastError();
-}
-
 // ----------------------------------------------------------------- LayerNorm
 // One wave64 per row of NV*256 floats: each lane holds NV float4.  Statistics
 // in float32: mean, then the mean of squared deviations (two passes over

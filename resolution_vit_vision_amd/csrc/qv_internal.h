@@ -104,7 +104,6 @@ hipError_t launch_setup_plan(const PlanEntry* host_plan_chunk, int count, int fi
                              hipStream_t s);
 hipError_t launch_rope_table(float2* tab, int positions, float theta, hipStream_t s);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
-hipError_t launch_warm(const void* src, size_t bytes, hipStream_t s);
 
 hipError_t launch_layernorm(const float* x, const float* g, const float* b, void* y, bool bf16, int rows,
                             int dim, float eps, hipStream_t s);
