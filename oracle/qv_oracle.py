@@ -24,6 +24,9 @@ title and section):
   fold        still images: the duplicated frame folded into a Conv2d
               weight summed over the temporal taps, K = C*14*14
               [LiteRT-LM card, Conversion notes: Conv3d -> Conv2d fold]
+  quantize    optional int8 weights of the block matrices: symmetric, one
+              scale per output channel [LiteRT-LM card, table rows Vision /
+              Adapter: int8 weights]
   patch_embed Conv3d with kernel = stride = (2,14,14) as a matrix product
   rope        2-D rotary positions over the (h, w) patch grid
               [Neurarch Qwen2-VL card, Structure table row "2D RoPE";
@@ -479,6 +482,35 @@ def vision_block_rows(z: np.ndarray, p: Dict[str, np.ndarray], cu_seqlens: np.nd
     zr = z[rows] + o @ p["proj_w"].T + p["proj_b"]
     a2 = layer_norm(zr, p["ln2_w"], p["ln2_b"], eps)
     return zr + quick_gelu(a2 @ p["fc1_w"].T + p["fc1_b"]) @ p["fc2_w"].T + p["fc2_b"]
+
+
+# ------------------------------------------------------------ int8 weights
+QUANT_KEYS = ("qkv_w", "proj_w", "fc1_w", "fc2_w")
+
+
+def quantize_i8(w: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Symmetric int8 weights with one float32 scale per output channel (row)
+    [LiteRT-LM card, table rows Vision / Adapter: int8 weights].  The card
+    fixes neither the grouping nor the rounding; reading: per row,
+    scale = max|w| / 127 (1 for an all-zero row), q = round half to even of
+    w / scale, clamped to [-127, 127]; every step in float32 (so the codes are
+    a plain function of the float32 weights, reproducible anywhere)."""
+    w32 = np.asarray(w, dtype=np.float32)
+    amax = np.max(np.abs(w32), axis=1)
+    scale = np.where(amax > 0, amax / np.float32(127.0), np.float32(1.0)).astype(np.float32)
+    q = np.clip(np.rint(w32 / scale[:, None]), -127, 127).astype(np.int8)
+    return q, scale
+
+
+def dequantized_params(params: Dict[str, np.ndarray], depth: int) -> Dict[str, np.ndarray]:
+    """The parameters with every block matrix replaced by q * scale (float64):
+    what an int8-weight tower computes with."""
+    out = dict(params)
+    for l in range(depth):
+        for k in QUANT_KEYS:
+            q, sc = quantize_i8(params[f"blocks.{l}.{k}"])
+            out[f"blocks.{l}.{k}"] = q.astype(np.float64) * sc.astype(np.float64)[:, None]
+    return out
 
 
 def block_params(params: Dict[str, np.ndarray], l: int, dtype=np.float64) -> Dict[str, np.ndarray]:

@@ -7,6 +7,7 @@ import math
 import os
 
 import numpy as np
+import synth
 import pytest
 import torch
 import torch.nn.functional as F
@@ -673,3 +674,49 @@ def test_normalize_closed_forms():
     # the CLIP constants of the processor table
     assert O.CLIP_MEAN == (0.48145466, 0.4578275, 0.40821073)
     assert O.CLIP_STD == (0.26862954, 0.26130258, 0.27577711)
+
+
+# ------------------------------------------------------------ int8 weights
+def test_quantize_i8_hand_example():
+    w = np.array([[0.5, -1.0, 0.25, 0.0],       # amax 1.0 -> scale 1/127
+                  [3.0, 1.5, -0.75, 2.25],       # amax 3.0 -> scale 3/127
+                  [0.0, 0.0, 0.0, 0.0]],         # all zero -> scale 1, codes 0
+                 dtype=np.float32)
+    q, s = O.quantize_i8(w)
+    assert s.dtype == np.float32 and q.dtype == np.int8
+    assert s[0] == np.float32(1.0) / np.float32(127) and s[1] == np.float32(3.0) / np.float32(127) and s[2] == 1
+    # 0.5 * 127 = 63.5 -> 64 (half to even), 0.25 * 127 = 31.75 -> 32; the
+    # largest magnitude of a row maps to +-127
+    assert q[0].tolist() == [64, -127, 32, 0]
+    assert q[1].tolist() == [127, 64, -32, 95]   # 1.5/3*127 = 63.5 -> 64; 2.25/3*127 = 95.25 -> 95
+    assert (q[2] == 0).all()
+
+
+def test_quantize_i8_error_bound_and_extremes():
+    rng = np.random.default_rng(31)
+    w = (rng.standard_normal((64, 300)) * 0.02).astype(np.float32)
+    q, s = O.quantize_i8(w)
+    err = np.abs(q.astype(np.float64) * s[:, None] - w)
+    # rounding to the nearest code: at most half a step (plus float32 slack)
+    assert (err <= s[:, None].astype(np.float64) * (0.5 + 1e-5)).all()
+    assert (np.abs(q).max(axis=1) == 127).all()      # each row's extreme is used
+    assert q.min() >= -127                           # -128 never appears
+    # the scale is per row: scaling one row leaves the others' codes alone
+    w2 = w.copy()
+    w2[3] *= 10
+    q2, s2 = O.quantize_i8(w2)
+    assert np.array_equal(np.delete(q2, 3, 0), np.delete(q, 3, 0)) and np.array_equal(q2[3], q[3])
+
+
+def test_dequantized_params_touch_only_block_matrices():
+    wl = synth.small_workload("q", [(56, 56, 1)], depth=2)
+    p = synth.params(wl)
+    d = O.dequantized_params(p, 2)
+    for k, v in p.items():
+        name = k.split(".")[-1]
+        if k.startswith("blocks.") and name in O.QUANT_KEYS:
+            q, s = O.quantize_i8(v)
+            assert np.array_equal(d[k], q.astype(np.float64) * s.astype(np.float64)[:, None])
+            assert not np.array_equal(d[k], v)
+        else:
+            assert d[k] is v
