@@ -129,6 +129,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fold", action="store_true",
                     help="keep the Conv3d patch-embed (K = 1176) for still images")
+    ap.add_argument("--weights", choices=("bf16", "int8"), default="bf16",
+                    help="block matrices as bf16, or int8 codes with a float32 scale per row")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
 
@@ -155,7 +157,9 @@ def main():
     imgs = synth.pixels(wl)
     fold = not args.no_fold and all(f == 1 for _, _, f in wl.images)
     enc = qv.Encoder(params, imgs, depth=wl.depth, out_dim=wl.out_dim, dtype=wl.dtype, window=wl.window,
-                     full_blocks=wl.full_blocks, fold=fold)
+                     full_blocks=wl.full_blocks, fold=fold,
+                     weights="int8" if args.weights == "int8" else "dtype")
+    tkey = wl.name + ("+int8" if args.weights == "int8" else "")
     grids = enc.grids
     n = enc.n
     m = n // 4
@@ -214,11 +218,11 @@ def main():
                     "flops_per_launch": per[dominant], "avg_launch_ms": dom_avg_ms, "launches": dom_launches,
                     "timing": "hipExtLaunchKernelGGL start/stop events around every launch of the class "
                               "(each interval also holds the launch's dispatch, ~3 us)",
-                    "traffic": traffic_for(dominant, wl.name)}
+                    "traffic": traffic_for(dominant, tkey)}
     else:
         roofline = {"bound": "hbm", "kernel": dominant, "achieved": None, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": None, "avg_launch_ms": dom_avg_ms, "launches": dom_launches,
-                    "traffic": traffic_for(dominant, wl.name)}
+                    "traffic": traffic_for(dominant, tkey)}
 
     result = {
         "metric": "merged vision tokens/sec",
@@ -239,7 +243,8 @@ def main():
                    + (["..."] if len(wl.images) > 4 else []),
                    "n_images": len(wl.images), "patches": n, "merged_tokens": m, "depth": wl.depth,
                    "out_dim": wl.out_dim, "window": wl.window, "full_blocks": list(wl.full_blocks),
-                   "patch_embed": "conv2d fold, K=592" if fold else "conv3d, K=1176"},
+                   "patch_embed": "conv2d fold, K=592" if fold else "conv3d, K=1176",
+                   "block_weights": "int8 per-row scales" if args.weights == "int8" else "bf16"},
         "patches_per_s": n * args.steps / (ms / 1e3),
         "algorithmic_tflop_per_step": flops / 1e12,
         "achieved_tflops": flops / (ms_per_step / 1e3) / 1e12,

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define QV_ABI_VERSION 2
+#define QV_ABI_VERSION 3
 
 typedef enum qv_status {
   QV_OK = 0,
@@ -62,8 +62,10 @@ typedef enum qv_status {
 
 typedef enum qv_dtype {
   QV_F32 = 0,  /* float32 operands and activations (correctness mode)         */
-  QV_BF16 = 1  /* bf16 GEMM/attention operands, float32 accumulation,
+  QV_BF16 = 1, /* bf16 GEMM/attention operands, float32 accumulation,
                   residual stream, LayerNorm statistics and softmax            */
+  QV_I8 = 2    /* weight format only: int8 codes [rows][cols] with one float32
+                  scale per row (qv_quantize_i8)                               */
 } qv_dtype;
 
 /* Text of the last non-OK status returned on the calling thread ("" if none). */
@@ -194,13 +196,18 @@ qv_status qv_fold_patch_weight(const void *w, int32_t dim, int32_t channels, int
 
 /* ---------------------------------------------------------- vision tower */
 
-/* Device pointers of one block.  Matrices in the tower dtype, vectors f32.
+/* Device pointers of one block.  Matrices in the tower dtype (int8 when
+ * qv_vision_cfg.weights is QV_I8), vectors f32.
  * qkv_w [3*dim][dim] rows = [q | k | v], each head-major (head h owns rows
  * 80h .. 80h+79 of its third); proj_w [dim][dim]; fc1_w [mlp][dim];
- * fc2_w [dim][mlp]. */
+ * fc2_w [dim][mlp].  With int8 weights the matrices are dense int8 codes
+ * (16-byte aligned) and qkv_s [3*dim], proj_s [dim], fc1_s [mlp],
+ * fc2_s [dim] their float32 row scales (weight = code * scale of its row);
+ * otherwise the four scale pointers are ignored and may be NULL. */
 typedef struct qv_block_w {
   const void *ln1_w, *ln1_b, *qkv_w, *qkv_b, *proj_w, *proj_b;
   const void *ln2_w, *ln2_b, *fc1_w, *fc1_b, *fc2_w, *fc2_b;
+  const float *qkv_s, *proj_s, *fc1_s, *fc2_s;
 } qv_block_w;
 
 /* patch_w: device [dim][patch_dim] (the Conv3d weight [dim][C][2][14][14]
@@ -234,7 +241,14 @@ typedef struct qv_vision_cfg {
    * the q/k/v layout, so small windows cost more q/k/v workspace than the
    * image layout (W = 8: none; W = 2: 16x). */
   int32_t window;
-  int32_t reserved0;  /* 0 */
+  /* Format of the four block matrices (LiteRT-LM card, model table, Vision
+   * and Adapter rows: int8 weights): 0 = the tower dtype; QV_I8 = int8 codes
+   * with a float32 scale per output row (qv_block_w).  An int8 product is
+   * out[m][n] = scale[n] * sum_k a[m][k] * code[n][k]: bf16 activations
+   * times the codes (exact in bf16), float32 accumulation, the scale applied
+   * to the float32 sum.  QV_I8 needs dtype QV_BF16, dim 1280 and mlp 5120.
+   * The patch-embed weight stays in the tower dtype. */
+  int32_t weights;
   uint64_t full_blocks;
 } qv_vision_cfg;
 
@@ -266,6 +280,19 @@ qv_status qv_vision_workspace_size(const qv_vision_cfg *c, const int32_t *grid_t
 qv_status qv_vision_forward(const qv_vision_cfg *c, const qv_vision_w *w, const void *patches,
                             const int32_t *grid_thw, int32_t n_img, const int32_t *cu_seqlens,
                             float *hidden, void *ws, size_t ws_bytes, void *stream);
+
+/* Symmetric per-row int8 weights (LiteRT-LM card, model table, Vision and
+ * Adapter rows: int8 weights; the grouping and rounding are this library's
+ * choice): for each row r, in float32, scale[r] = max_c |w[r][c]| / 127
+ * (1 when the row is all zeros) and q[r][c] = w[r][c] / scale[r] rounded
+ * half to even and clamped to [-127, 127].
+ * w: device [rows][ld] in dtype (QV_F32 or QV_BF16, read exactly);
+ * q: device out int8 [rows][cols] (dense); scale: device out float32
+ * [rows].  Errors: QV_ERR_NULL, QV_ERR_SHAPE (rows, cols <= 0 or
+ * ld < cols), QV_ERR_UNSUPPORTED (dtype), QV_ERR_HIP.  Outputs must not
+ * overlap w. */
+qv_status qv_quantize_i8(const void *w, int32_t rows, int32_t cols, int32_t ld, qv_dtype dtype, int8_t *q,
+                         float *scale, void *stream);
 
 /* ---------------------------------------------------------- patch merger */
 

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(HERE, "libqv.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "qv.h")
 
 QV_OK, QV_ERR_NULL, QV_ERR_SHAPE, QV_ERR_BUDGET, QV_ERR_WORKSPACE, QV_ERR_UNSUPPORTED, QV_ERR_HIP = range(7)
-QV_F32, QV_BF16 = 0, 1
+QV_F32, QV_BF16, QV_I8 = 0, 1, 2
 STATUS_NAMES = {0: "QV_OK", 1: "QV_ERR_NULL", 2: "QV_ERR_SHAPE", 3: "QV_ERR_BUDGET", 4: "QV_ERR_WORKSPACE",
                 5: "QV_ERR_UNSUPPORTED", 6: "QV_ERR_HIP"}
 
@@ -49,8 +49,13 @@ BLOCK_FIELDS = ("ln1_w", "ln1_b", "qkv_w", "qkv_b", "proj_w", "proj_b",
                 "ln2_w", "ln2_b", "fc1_w", "fc1_b", "fc2_w", "fc2_b")
 
 
+# float32 row scales of the int8 block matrices (qv_vision_cfg.weights = QV_I8)
+BLOCK_SCALE_FIELDS = ("qkv_s", "proj_s", "fc1_s", "fc2_s")
+QUANT_FIELDS = ("qkv_w", "proj_w", "fc1_w", "fc2_w")
+
+
 class BlockW(Structure):
-    _fields_ = [(k, c_void_p) for k in BLOCK_FIELDS]
+    _fields_ = [(k, c_void_p) for k in BLOCK_FIELDS + BLOCK_SCALE_FIELDS]
 
 
 class VisionW(Structure):
@@ -60,7 +65,7 @@ class VisionW(Structure):
 class VisionCfg(Structure):
     _fields_ = [("depth", c_int32), ("dim", c_int32), ("heads", c_int32), ("mlp", c_int32),
                 ("patch_dim", c_int32), ("ld", c_int32), ("merge", c_int32), ("dtype", c_int32),
-                ("ln_eps", c_float), ("rope_theta", c_float), ("window", c_int32), ("reserved0", c_int32),
+                ("ln_eps", c_float), ("rope_theta", c_float), ("window", c_int32), ("weights", c_int32),
                 ("full_blocks", c_uint64)]
 
 
@@ -117,6 +122,8 @@ def lib() -> ctypes.CDLL:
     L.qv_fold_patch_weight.restype = c_int32
     L.qv_fold_patch_weight.argtypes = [c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p, c_int32,
                                        c_int32, c_void_p]
+    L.qv_quantize_i8.restype = c_int32
+    L.qv_quantize_i8.argtypes = [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p]
     L.qv_vision_workspace_size.restype = c_int32
     L.qv_vision_workspace_size.argtypes = [POINTER(VisionCfg), c_void_p, c_int32, POINTER(c_size_t)]
     L.qv_vision_forward.restype = c_int32

@@ -138,7 +138,7 @@ struct EpiStoreF32 {
     *reinterpret_cast<float4*>(C + (size_t)row * ldc + col) = make_float4(v[0], v[1], v[2], v[3]);
   }
   template <int FM, int FN>
-  __device__ void apply_staged(f32x16 (&acc)[FM][FN], float* wlds, int wm0, int wn0, int lane, int M, int N) const {
+  __device__ __forceinline__ void apply_staged(f32x16 (&acc)[FM][FN], float* wlds, int wm0, int wn0, int lane, int M, int N) const {
     staged_store<4>(*this, acc, wlds, wm0, wn0, lane, M, N);
   }
   template <int FM, int FN>
@@ -175,7 +175,7 @@ struct EpiPartF32 {
     *reinterpret_cast<float4*>(C + (size_t)row * ldc + col) = make_float4(v[0], v[1], v[2], v[3]);
   }
   template <int FM, int FN>
-  __device__ void apply_staged(f32x16 (&acc)[FM][FN], float* wlds, int wm0, int wn0, int lane, int M, int N) const {
+  __device__ __forceinline__ void apply_staged(f32x16 (&acc)[FM][FN], float* wlds, int wm0, int wn0, int lane, int M, int N) const {
     staged_store<4>(*this, acc, wlds, wm0, wn0, lane, M, N);
   }
 };
@@ -202,7 +202,7 @@ struct EpiResidF32 {
         make_float4(z.x + v[0], z.y + v[1], z.z + v[2], z.w + v[3]);
   }
   template <int FM, int FN>
-  __device__ void apply_staged(f32x16 (&acc)[FM][FN], float* wlds, int wm0, int wn0, int lane, int M, int N) const {
+  __device__ __forceinline__ void apply_staged(f32x16 (&acc)[FM][FN], float* wlds, int wm0, int wn0, int lane, int M, int N) const {
     staged_store<4>(*this, acc, wlds, wm0, wn0, lane, M, N);
   }
   template <int FM, int FN>
@@ -247,7 +247,7 @@ struct EpiActBf16 {
     *reinterpret_cast<uint4*>(C + (size_t)row * ldc + col) = pk;
   }
   template <int FM, int FN>
-  __device__ void apply_staged(f32x16 (&acc)[FM][FN], float* wlds, int wm0, int wn0, int lane, int M, int N) const {
+  __device__ __forceinline__ void apply_staged(f32x16 (&acc)[FM][FN], float* wlds, int wm0, int wn0, int lane, int M, int N) const {
     staged_store<8>(*this, acc, wlds, wm0, wn0, lane, M, N);
   }
   template <int FM, int FN>
@@ -313,7 +313,7 @@ struct EpiQkv {
   // As in staged_store, every global load (bias, token info, rotary table)
   // of a 32-row block is issued before that block's first store.
   template <int FM, int FN>
-  __device__ void apply_staged(f32x16 (&acc)[FM][FN], float* wlds, int wm0, int wn0, int lane, int M, int N) const {
+  __device__ __forceinline__ void apply_staged(f32x16 (&acc)[FM][FN], float* wlds, int wm0, int wn0, int lane, int M, int N) const {
     const int dim = o.dim;
     const int c = lane & 31;
     if (wn0 < 2 * dim) {
@@ -740,6 +740,119 @@ hipError_t gemm_bf16_act_bf16(const void* A, int lda, const void* B, int ldb, in
 hipError_t gemm_bf16_qkv(const void* A, int lda, const void* B, int ldb, int M, int K, const float* bias,
                          const QkvOut& o, hipStream_t s) {
   return run_bf16(A, lda, B, ldb, M, 3 * o.dim, K, EpiQkv{o, bias}, RowMapQkv{o.dim}, s);
+}
+
+// ============================================== int8 weights (bf16 path)
+// C[m][n] = scale[n] * sum_k A[m][k] q[n][k] with int8 q [N][ldb] and one
+// float32 scale per row of q, through k_gemm_ws_i8 (codes converted to bf16
+// by producer waves, scales applied to the accumulators).  Tilings: 128x128
+// for q/k/v (the rotation epilogue needs 64-wide wave tiles), 128x160
+// otherwise, two A-DMA and two B-convert waves each, with the K range split
+// into runs when the tile count is small (the runs' partial sums then go to
+// the next LayerNorm).
+template <int BM, int BN, int WM, int WN, int ST, int KT, class Epi, class RowMap>
+static hipError_t launch_ws_i8(const void* A, int lda, const int8_t* B, int ldb, const float* scale, int M, int N,
+                               const Epi& epi, RowMap rmap, hipStream_t s, int splits = 1) {
+  constexpr int NPA = 2, NPB = 2;
+  const XcdCut cut = xcd_cut((M + BM - 1) / BM, (N + BN - 1) / BN, BM, BN);
+  QV_KLAUNCH((k_gemm_ws_i8<BM, BN, WM, WN, ST, KT, NPA, NPB, Epi, RowMap>), dim3(cut.grid, (unsigned)splits),
+             dim3((WM * WN + NPA + NPB) * 64), 0, s, reinterpret_cast<const uint16_t*>(A), lda, B, ldb, scale, M, N,
+             cut.xgn, 8, epi, rmap);
+  return hipGetLastError();
+}
+
+static bool i8_shape_ok(const void* A, int lda, int ldb, int N, int K, int nmul) {
+  return A && lda % 8 == 0 && ldb % 16 == 0 && N % nmul == 0 && K % 64 == 0;
+}
+
+hipError_t gemm_i8w_qkv(const void* A, int lda, const int8_t* B, int ldb, const float* scale, int M, int K,
+                        const float* bias, const QkvOut& o, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  if (!i8_shape_ok(A, lda, ldb, 3 * o.dim, K, 128) || K != 1280) return hipErrorInvalidValue;
+  return launch_ws_i8<128, 128, 4, 2, 4, 20>(A, lda, B, ldb, scale, M, 3 * o.dim, EpiQkv{o, bias},
+                                                RowMapQkv{o.dim}, s);
+}
+
+hipError_t gemm_i8w_act_bf16(const void* A, int lda, const int8_t* B, int ldb, const float* scale, int M, int N,
+                             int K, const float* bias, Act act, void* C, int ldc, hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (!i8_shape_ok(A, lda, ldb, N, K, 160) || K != 1280 || act != Act::QuickGelu) return hipErrorInvalidValue;
+  return launch_ws_i8<128, 160, 4, 1, 4, 20>(A, lda, B, ldb, scale, M, N,
+                                                EpiActBf16<Act::QuickGelu>{(uint16_t*)C, ldc, bias},
+                                                RowMapIdentity{}, s);
+}
+
+// K runs for an int8-weight GEMM of N = 1280 (1 = no split): the largest of
+// 4 and 2 whose workgroups still fit one per CU.
+int gemm_i8w_runs(int M, int N, int K) {
+  if (N % 160 || K % 64) return 1;
+  const int64_t tiles = (int64_t)((M + 127) / 128) * (N / 160);
+  const int kt = K / 64;
+  for (int s : {4, 2})
+    if (tiles * s <= 256 && kt % s == 0 && (kt / s == 20 || kt / s == 10 || kt / s == 5)) return s;
+  return 1;
+}
+
+hipError_t gemm_i8w_splitk_f32(const void* A, int lda, const int8_t* B, int ldb, const float* scale, int M, int N,
+                               int K, int splits, float* P, hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (!i8_shape_ok(A, lda, ldb, N, K, 160) || (splits != 2 && splits != 4) || (K / 64) % splits)
+    return hipErrorInvalidValue;
+  const EpiPartF32 e{P, N, (size_t)M * N};
+  switch (K / 64 / splits) {
+    case 20: return launch_ws_i8<128, 160, 4, 1, 4, 20>(A, lda, B, ldb, scale, M, N, e, RowMapIdentity{}, s, splits);
+    case 10: return launch_ws_i8<128, 160, 4, 1, 4, 10>(A, lda, B, ldb, scale, M, N, e, RowMapIdentity{}, s, splits);
+    case 5: return launch_ws_i8<128, 160, 4, 1, 4, 5>(A, lda, B, ldb, scale, M, N, e, RowMapIdentity{}, s, splits);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t gemm_i8w_resid_f32(const void* A, int lda, const int8_t* B, int ldb, const float* scale, int M, int N,
+                              int K, const float* bias, float* Z, int ldz, hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (!i8_shape_ok(A, lda, ldb, N, K, 160)) return hipErrorInvalidValue;
+  const EpiResidF32 e{Z, ldz, bias};
+  switch (K / 64) {
+    case 20: return launch_ws_i8<128, 160, 4, 1, 4, 20>(A, lda, B, ldb, scale, M, N, e, RowMapIdentity{}, s);
+    case 80: return launch_ws_i8<128, 160, 4, 1, 4, 80>(A, lda, B, ldb, scale, M, N, e, RowMapIdentity{}, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Symmetric per-row int8: scale = max|w| / 127 (1 for an all-zero row),
+// q = round half to even of w / scale clamped to +-127, all in float32.
+// One 256-thread workgroup per row.
+__global__ __launch_bounds__(256) void k_quantize_i8(const void* __restrict__ w, int cols, int ld, int bf16,
+                                                     int8_t* __restrict__ q, float* __restrict__ scale) {
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  auto load = [&](int c) -> float {
+    const size_t i = (size_t)row * ld + c;
+    return bf16 ? __builtin_bit_cast(float, (uint32_t)reinterpret_cast<const uint16_t*>(w)[i] << 16)
+                : reinterpret_cast<const float*>(w)[i];
+  };
+  float amax = 0.f;
+  for (int c = tid; c < cols; c += 256) amax = fmaxf(amax, fabsf(load(c)));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  __shared__ float wmax[4];
+  if ((tid & 63) == 0) wmax[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const float sc = amax > 0.f ? amax / 127.0f : 1.0f;
+  if (tid == 0) scale[row] = sc;
+  for (int c = tid; c < cols; c += 256) {
+    float v = __builtin_rintf(load(c) / sc);
+    v = fminf(fmaxf(v, -127.f), 127.f);
+    q[(size_t)row * cols + c] = (int8_t)(int)v;
+  }
+}
+
+hipError_t launch_quantize_i8(const void* w, int rows, int cols, int ld, bool bf16, int8_t* q, float* scale,
+                              hipStream_t s) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  QV_KLAUNCH(k_quantize_i8, dim3((unsigned)rows), dim3(256), 0, s, w, cols, ld, bf16 ? 1 : 0, q, scale);
+  return hipGetLastError();
 }
 
 // =================================================== float32 (correctness)

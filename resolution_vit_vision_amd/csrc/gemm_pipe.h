@@ -422,4 +422,208 @@ __global__ __launch_bounds__((WM * WN + NP) * 64) void k_gemm_ws(const uint16_t*
   epi.apply_staged(acc, slot, m0 + wm * C::TM, n0 + wn * C::TN, lane, M, N);
 }
 
+// ------------------------------------------- int8 weights (warp-specialized)
+// Same ring and consumers as k_gemm_ws; B is int8 codes q [N][ldb] with one
+// float32 scale s per row.  Because s belongs to an output column,
+// C[m][n] = s[n] * sum_k A[m][k] q[n][k]: the ring holds the codes themselves
+// as bf16 (exact, |q| <= 127) and the consumers multiply their accumulators
+// by s before the epilogue, which is unchanged.
+//
+// Two kinds of producer waves.  NPA waves move A by LDS-DMA exactly as in
+// k_gemm_ws.  NPB waves fetch B with 16-byte global loads (16 codes of one
+// row) into registers, STAGES stages ahead, and at step kt convert B(kt + 1)
+// (one sign-extending byte convert per code, one pack per pair) and write it
+// to its ring buffer, so the conversion overlaps the wait for A(kt).  The
+// roles stay in separate waves because a wave that writes LDS while its own
+// LDS-DMA loads are in flight gets a wait for all of them from the compiler.
+
+// Two floats to one dword of bf16, round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16_pair(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// A-only producer wave: its 1 KB blocks of the A tile (same swizzle as ws_setup).
+template <int BM, int NPA, int LPA>
+__device__ __forceinline__ void i8_a_setup(const char* (&gsrc)[LPA], uint32_t (&ldst)[LPA], const uint16_t* A,
+                                           int lda, int M, int m0, int pw, int lane) {
+#pragma unroll
+  for (int i = 0; i < LPA; ++i) {
+    const int blk = i * NPA + pw;
+    const int q = blk * 64 + lane;
+    const int r = q >> 3;
+    int g = m0 + r;
+    g = g < M ? g : M - 1;
+    gsrc[i] = reinterpret_cast<const char*>(A + (size_t)g * lda + swz_chunk(r, q & 7) * 8);
+    ldst[i] = (uint32_t)(blk * 1024);
+  }
+}
+
+// B producer wave.  Items are (row r, group j of 16 codes = two 16-byte bf16
+// chunks in LDS); a stage has BN * 4 of them, split evenly over the NPB * 64
+// lanes (four lanes read one row's 64 bytes).  The waits for the B
+// registers are the compiler's (plain loads into registers).
+template <int BM, int BN, int NPB, int STAGES, int KT, class RowMap>
+struct I8BProd {
+  static constexpr int ITEMS = BN * 4;
+  static constexpr int LB = ITEMS / (NPB * 64);
+  static_assert(ITEMS % (NPB * 64) == 0, "whole items per producer lane");
+  static_assert(STAGES >= 3, "B(kt + 1) is written while the consumers read stage kt - 1");
+  uint16_t* const* st;
+  const int8_t* bsrc[LB];
+  uint32_t bdst0[LB], bdst1[LB];
+  uint4 breg[STAGES][LB];
+
+  __device__ __forceinline__ void setup(uint16_t* const* st_, const int8_t* B, int ldb, int N, int n0, int pw,
+                                        int lane, RowMap rmap) {
+    st = st_;
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+      const int item = (i * NPB + pw) * 64 + lane;
+      const int r = item >> 2, j = item & 3;
+      int g = n0 + r;
+      g = g < N ? g : N - 1;
+      bsrc[i] = B + (size_t)rmap(g) * ldb + 16 * j;
+      const uint32_t rowb = (uint32_t)(BM * 64 * 2 + r * 128);
+      bdst0[i] = rowb + ((uint32_t)swz_chunk(r, 2 * j) << 4);
+      bdst1[i] = rowb + ((uint32_t)swz_chunk(r, 2 * j + 1) << 4);
+    }
+  }
+  template <int j>
+  __device__ __forceinline__ void issue() {
+    if constexpr (j < KT) {
+#pragma unroll
+      for (int i = 0; i < LB; ++i) breg[j % STAGES][i] = *reinterpret_cast<const uint4*>(bsrc[i] + (size_t)j * 64);
+    }
+  }
+  // codes of stage j -> bf16 in its ring buffer, in the layout the DMA gives A
+  template <int j>
+  __device__ __forceinline__ void convert() {
+    char* base = reinterpret_cast<char*>(st[j % STAGES]);
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+      const uint4 w = breg[j % STAGES][i];
+      const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+      uint32_t pk[8];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const float f0 = (float)(int8_t)wd[d];
+        const float f1 = (float)(int8_t)(wd[d] >> 8);
+        const float f2 = (float)(int8_t)(wd[d] >> 16);
+        const float f3 = (float)((int32_t)wd[d] >> 24);
+        pk[2 * d] = pack_bf16_pair(f0, f1);
+        pk[2 * d + 1] = pack_bf16_pair(f2, f3);
+      }
+      *reinterpret_cast<uint4*>(base + bdst0[i]) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+      *reinterpret_cast<uint4*>(base + bdst1[i]) = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+    }
+  }
+  // step kt: B(kt + 1) into its buffer (free: the consumers finished stage
+  // kt + 1 - STAGES before barrier kt - 1), its registers refilled with
+  // B(kt + 1 + STAGES); then barrier kt, which publishes B(kt) (written a
+  // step earlier) together with the A producers' stage kt
+  template <int kt>
+  __device__ __forceinline__ void step() {
+    if constexpr (kt < KT) {
+      if constexpr (kt + 1 < KT) {
+        convert<kt + 1>();
+        issue<kt + 1 + STAGES>();
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+      QV_BARRIER();
+      step<kt + 1>();
+    }
+  }
+  __device__ __forceinline__ void run() {
+    issue<0>();
+    issue<1>();
+    issue<2>();
+    if constexpr (STAGES > 3) issue<3>();
+    convert<0>();
+    issue<STAGES>();
+    step<0>();
+  }
+};
+
+template <int BM, int BN, int WM, int WN, int STAGES, int KT, int NPA, int NPB, class Epi, class RowMap>
+__global__ __launch_bounds__((WM * WN + NPA + NPB) * 64) void k_gemm_ws_i8(
+    const uint16_t* __restrict__ A, int lda, const int8_t* __restrict__ B, int ldb, const float* __restrict__ bscale,
+    int M, int N, int xgn, int group, Epi epi_all, RowMap rmap) {
+  using C = PipeCfg<BM, BN, WM, WN, STAGES, 1>;
+  constexpr int NC = WM * WN;
+  constexpr int ABLK = BM * 8 / 64;
+  constexpr int LPA = ABLK / NPA;
+  static_assert(ABLK % NPA == 0, "A blocks split evenly over the A producers");
+  static_assert(LPA * (STAGES - 1) <= 63, "A loads in flight fit the 6-bit vmcnt");
+  static_assert(STAGES == 3 || STAGES == 4, "3 or 4 stages");
+  constexpr int SE = C::STAGE_ELEMS;
+  __shared__ __attribute__((aligned(1024))) uint16_t st0[SE];
+  __shared__ __attribute__((aligned(1024))) uint16_t st1[SE];
+  __shared__ __attribute__((aligned(1024))) uint16_t st2[SE];
+  __shared__ __attribute__((aligned(1024))) uint16_t st3[STAGES > 3 ? SE : 8];
+  uint16_t* const st[8] = {st0, st1, st2, st3, st0, st0, st0, st0};
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tiles_n = (N + BN - 1) / BN, tiles_m = (M + BM - 1) / BM;
+  int tm, tn;
+  if (!tile_coords(blockIdx.x, tiles_m, tiles_n, xgn, group, tm, tn)) return;  // uniform over the workgroup
+  const int m0 = tm * BM, n0 = tn * BN;
+  A += (size_t)blockIdx.y * KT * 64;
+  B += (size_t)blockIdx.y * KT * 64;
+  const Epi epi = epi_at_split(epi_all, (int)blockIdx.y);
+
+  if (wave >= NC + NPA) {
+    I8BProd<BM, BN, NPB, STAGES, KT, RowMap> p;
+    p.setup(st, B, ldb, N, n0, wave - NC - NPA, lane, rmap);
+    p.run();
+    QV_BARRIER();  // pairs with the consumers' end-of-loop barrier
+    return;
+  }
+  if (wave >= NC) {
+    const char* gsrc[LPA];
+    uint32_t ldst[LPA];
+    i8_a_setup<BM, NPA, LPA>(gsrc, ldst, A, lda, M, m0, wave - NC, lane);
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+      if (s < KT) ws_issue<LPA>(gsrc, ldst, st[s], s);
+    WsProducer<KT, STAGES, LPA>::template run<0>(st, gsrc, ldst);
+    QV_BARRIER();
+    return;
+  }
+
+  const int wm = wave / WN, wn = wave % WN;
+  // this lane's output columns' weight-row scales, fetched before the loop
+  float sc[C::FN];
+#pragma unroll
+  for (int fn = 0; fn < C::FN; ++fn) {
+    const int col = n0 + wn * C::TN + fn * 32 + (lane & 31);
+    sc[fn] = col < N ? bscale[rmap(col)] : 0.f;
+  }
+  f32x16 acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  WsConsumer<C, KT, STAGES>::template run<0>(st, acc, wm, wn, lane);
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] *= sc[j];
+
+  constexpr int SLOT = Epi::kPatchFloats;
+  constexpr int PER = (SE * 2) / (SLOT * 4);
+  static_assert(PER >= 1 && PER * STAGES >= NC, "per-wave slots fit in the ring");
+  QV_BARRIER();
+  const int sb = wave / PER;
+  uint16_t* sbuf = sb == 0 ? st0 : sb == 1 ? st1 : sb == 2 ? st2 : st3;
+  float* slot = reinterpret_cast<float*>(sbuf) + (wave % PER) * SLOT;
+  epi.apply_staged(acc, slot, m0 + wm * C::TM, n0 + wn * C::TN, lane, M, N);
+}
+
 }  // namespace qv

@@ -298,6 +298,17 @@ qv_status qv_fold_patch_weight(const void* w, int32_t dim, int32_t channels, int
   return QV_OK;
 }
 
+qv_status qv_quantize_i8(const void* w, int32_t rows, int32_t cols, int32_t ld, qv_dtype dtype, int8_t* q,
+                         float* scale, void* stream) {
+  if (!w || !q || !scale) return fail(QV_ERR_NULL, "w, q and scale must be non-NULL");
+  if (dtype != QV_F32 && dtype != QV_BF16) return fail(QV_ERR_UNSUPPORTED, "w must be QV_F32 or QV_BF16, not %d", (int)dtype);
+  if (rows <= 0 || cols <= 0 || ld < cols) return fail(QV_ERR_SHAPE, "rows %d, cols %d must be positive and ld %d >= cols",
+                                                       rows, cols, ld);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  QV_HIP(launch_quantize_i8(w, rows, cols, ld, dtype == QV_BF16, q, scale, s));
+  return QV_OK;
+}
+
 }  // extern "C"
 
 // ------------------------------------------------------------------ encoder
@@ -315,7 +326,9 @@ struct VisionPlan {
   std::vector<ImgDesc> desc;
   std::vector<PlanEntry> plan;
   // windowed attention: a second padded layout with one kSeqAlign-row slot per window
-  int split_fc2 = 1;  // split-K runs of fc2 (bf16, small M)
+  int split_fc2 = 1;   // split-K runs of fc2 (bf16, small M)
+  int split_proj = 1;  // split-K runs of the out-projection (int8 weights, small M)
+  bool i8 = false;     // int8 block matrices
   int window = 0;
   int win_slot = 0;  // padded rows per window: kWinSlot (64) for W <= 8, else kSeqAlign (128)
   int64_t n_win = 0, Pw = 0;
@@ -342,7 +355,10 @@ qv_status check_vision_cfg(const qv_vision_cfg* c) {
   if (!(c->ln_eps >= 0.f) || !(c->rope_theta > 0.f)) return fail(QV_ERR_SHAPE, "ln_eps >= 0 and rope_theta > 0 required");
   if (c->window < 0 || c->window % c->merge || c->window > 10)
     return fail(QV_ERR_UNSUPPORTED, "window %d must be 0 or a multiple of merge %d in [2, 10]", c->window, c->merge);
-  if (c->reserved0 != 0) return fail(QV_ERR_SHAPE, "reserved0 must be 0");
+  if (c->weights != 0 && c->weights != QV_I8)
+    return fail(QV_ERR_UNSUPPORTED, "weights %d must be 0 or QV_I8", c->weights);
+  if (c->weights == QV_I8 && (c->dtype != QV_BF16 || c->dim != 1280 || c->mlp != 5120))
+    return fail(QV_ERR_UNSUPPORTED, "int8 weights need dtype QV_BF16, dim 1280 and mlp 5120");
   return QV_OK;
 }
 
@@ -436,14 +452,21 @@ qv_status make_plan(const qv_vision_cfg* c, const int32_t* grid_thw, int32_t n_i
   vp.off_h = o;    o = align_up(o + N * c->mlp * es);
   vp.off_qkv = o;
   if (c->dtype == QV_F32) o = align_up(o + N * 3 * c->dim * sizeof(float));
-  if (c->dtype == QV_BF16 && c->dim == 1280 && c->depth > 0) {
+  vp.i8 = c->weights == QV_I8;
+  if (vp.i8 && c->depth > 0) {
+    // int8 weights use 128 x 160 tiles: at small M the out-projection has
+    // too few of them unsplit, so both it and fc2 leave partial sums
+    vp.split_fc2 = gemm_i8w_runs((int)N, c->dim, c->mlp);
+    vp.split_proj = gemm_i8w_runs((int)N, c->dim, c->dim);
+  } else if (c->dtype == QV_BF16 && c->dim == 1280 && c->depth > 0) {
     // fc2 only: the out-projection's K = 1280 is too short for its split to
     // pay for the partial sums the LayerNorm reads back (measured 10.8 + 7.8
     // us against 11.9 + 4.2 us at 448x448)
     vp.split_fc2 = gemm_splitk_runs((int)N, c->dim, c->mlp);
   }
   vp.off_part = o;
-  if (vp.split_fc2 > 1) o = align_up(o + (size_t)vp.split_fc2 * N * c->dim * sizeof(float));
+  const int max_split = std::max(vp.split_fc2, vp.split_proj);
+  if (max_split > 1) o = align_up(o + (size_t)max_split * N * c->dim * sizeof(float));
   if (vp.window) {
     vp.off_tokw = o;   o = align_up(o + N * sizeof(int2));
     vp.off_outrow = o; o = align_up(o + (size_t)vp.Pw * sizeof(int32_t));
@@ -453,11 +476,17 @@ qv_status make_plan(const qv_vision_cfg* c, const int32_t* grid_thw, int32_t n_i
   return QV_OK;
 }
 
-qv_status check_block(const qv_block_w& b, int l) {
-  const void* p[] = {b.ln1_w, b.ln1_b, b.qkv_w, b.qkv_b, b.proj_w, b.proj_b,
-                     b.ln2_w, b.ln2_b, b.fc1_w, b.fc1_b, b.fc2_w, b.fc2_b};
-  for (int i = 0; i < 12; ++i)
+qv_status check_block(const qv_block_w& b, int l, bool i8) {
+  const void* p[] = {b.ln1_w, b.ln1_b, b.qkv_w, b.qkv_b, b.proj_w, b.proj_b, b.ln2_w, b.ln2_b,
+                     b.fc1_w, b.fc1_b, b.fc2_w, b.fc2_b, b.qkv_s, b.proj_s, b.fc1_s, b.fc2_s};
+  const int n = i8 ? 16 : 12;
+  for (int i = 0; i < n; ++i)
     if (!p[i]) return fail(QV_ERR_NULL, "block %d: weight pointer %d is NULL", l, i);
+  if (i8) {
+    const void* m[] = {b.qkv_w, b.proj_w, b.fc1_w, b.fc2_w};
+    for (const void* x : m)
+      if (reinterpret_cast<uintptr_t>(x) & 15) return fail(QV_ERR_SHAPE, "block %d: int8 matrices must be 16-byte aligned", l);
+  }
   return QV_OK;
 }
 
@@ -485,7 +514,7 @@ qv_status qv_vision_forward(const qv_vision_cfg* c, const qv_vision_w* w, const 
   if (!w->patch_w) return fail(QV_ERR_NULL, "patch_w is NULL");
   if (c->depth > 0 && !w->blocks) return fail(QV_ERR_NULL, "blocks is NULL");
   for (int l = 0; l < c->depth; ++l) {
-    st = check_block(w->blocks[l], l);
+    st = check_block(w->blocks[l], l, vp.i8);
     if (st != QV_OK) return st;
   }
   if (ws_bytes < vp.total)
@@ -582,12 +611,25 @@ qv_status qv_vision_forward(const qv_vision_cfg* c, const qv_vision_w* w, const 
     qv_status lst = layer_norm(b.ln1_w, b.ln1_b);
     if (lst != QV_OK) return lst;
     if (bf) {
-      QV_LAUNCH(QV_KC_QKV, s, gemm_bf16_qkv(A, D, b.qkv_w, D, M, D, (const float*)b.qkv_b, qb, s));
+      if (vp.i8)
+        QV_LAUNCH(QV_KC_QKV, s, gemm_i8w_qkv(A, D, (const int8_t*)b.qkv_w, D, b.qkv_s, M, D, (const float*)b.qkv_b, qb, s));
+      else
+        QV_LAUNCH(QV_KC_QKV, s, gemm_bf16_qkv(A, D, b.qkv_w, D, M, D, (const float*)b.qkv_b, qb, s));
       if (win && vp.win_slot == kWinSlot)
         QV_LAUNCH(QV_KC_ATTENTION, s, attention_bf16_windows(aw, s));
       else
         QV_LAUNCH(QV_KC_ATTENTION, s, attention_bf16(ab, s));
-      QV_LAUNCH(QV_KC_PROJ, s, gemm_bf16_resid_f32(O, D, b.proj_w, D, M, D, D, (const float*)b.proj_b, hidden, D, s));
+      if (vp.i8 && vp.split_proj > 1) {
+        QV_LAUNCH(QV_KC_PROJ, s, gemm_i8w_splitk_f32(O, D, (const int8_t*)b.proj_w, D, b.proj_s, M, D, D, vp.split_proj,
+                                                     part, s));
+        pending = vp.split_proj;
+        pending_bias = (const float*)b.proj_b;
+      } else if (vp.i8) {
+        QV_LAUNCH(QV_KC_PROJ, s, gemm_i8w_resid_f32(O, D, (const int8_t*)b.proj_w, D, b.proj_s, M, D, D,
+                                                    (const float*)b.proj_b, hidden, D, s));
+      } else {
+        QV_LAUNCH(QV_KC_PROJ, s, gemm_bf16_resid_f32(O, D, b.proj_w, D, M, D, D, (const float*)b.proj_b, hidden, D, s));
+      }
     } else {
       float* qkv = reinterpret_cast<float*>(base + vp.off_qkv);
       QV_LAUNCH(QV_KC_QKV, s, gemm_f32_store((const float*)A, D, (const float*)b.qkv_w, D, M, 3 * D, D, (const float*)b.qkv_b, qkv,
@@ -599,7 +641,19 @@ qv_status qv_vision_forward(const qv_vision_cfg* c, const qv_vision_w* w, const 
     }
     lst = layer_norm(b.ln2_w, b.ln2_b);
     if (lst != QV_OK) return lst;
-    if (bf) {
+    if (bf && vp.i8) {
+      QV_LAUNCH(QV_KC_FC1, s, gemm_i8w_act_bf16(A, D, (const int8_t*)b.fc1_w, D, b.fc1_s, M, F, D, (const float*)b.fc1_b,
+                                                Act::QuickGelu, H, F, s));
+      if (vp.split_fc2 > 1) {
+        QV_LAUNCH(QV_KC_FC2, s, gemm_i8w_splitk_f32(H, F, (const int8_t*)b.fc2_w, F, b.fc2_s, M, D, F, vp.split_fc2,
+                                                    part, s));
+        pending = vp.split_fc2;
+        pending_bias = (const float*)b.fc2_b;
+      } else {
+        QV_LAUNCH(QV_KC_FC2, s, gemm_i8w_resid_f32(H, F, (const int8_t*)b.fc2_w, F, b.fc2_s, M, D, F,
+                                                   (const float*)b.fc2_b, hidden, D, s));
+      }
+    } else if (bf) {
       QV_LAUNCH(QV_KC_FC1, s, gemm_bf16_act_bf16(A, D, b.fc1_w, D, M, F, D, (const float*)b.fc1_b, Act::QuickGelu, H, F, s));
       if (vp.split_fc2 > 1) {
         QV_LAUNCH(QV_KC_FC2, s, gemm_bf16_splitk_f32(H, F, b.fc2_w, F, M, D, F, vp.split_fc2, part, s));

@@ -132,6 +132,18 @@ hipError_t gemm_bf16_store_f32(const void* A, int lda, const void* B, int ldb, i
                                const float* bias, float* C, int ldc, hipStream_t s);
 hipError_t gemm_bf16_resid_f32(const void* A, int lda, const void* B, int ldb, int M, int N, int K,
                                const float* bias, float* Z, int ldz, hipStream_t s);
+// int8 weights (one float32 scale per weight row), bf16 activations.
+hipError_t gemm_i8w_qkv(const void* A, int lda, const int8_t* B, int ldb, const float* scale, int M, int K,
+                        const float* bias, const QkvOut& o, hipStream_t s);
+hipError_t gemm_i8w_act_bf16(const void* A, int lda, const int8_t* B, int ldb, const float* scale, int M, int N,
+                             int K, const float* bias, Act act, void* C, int ldc, hipStream_t s);
+int gemm_i8w_runs(int M, int N, int K);
+hipError_t gemm_i8w_splitk_f32(const void* A, int lda, const int8_t* B, int ldb, const float* scale, int M, int N,
+                               int K, int splits, float* P, hipStream_t s);
+hipError_t gemm_i8w_resid_f32(const void* A, int lda, const int8_t* B, int ldb, const float* scale, int M, int N,
+                              int K, const float* bias, float* Z, int ldz, hipStream_t s);
+hipError_t launch_quantize_i8(const void* w, int rows, int cols, int ld, bool bf16, int8_t* q, float* scale,
+                              hipStream_t s);
 // Split-K with the reduction left to launch_layernorm_acc: returns the number
 // of K runs that fills the GPU for this shape (1 = no split).
 int gemm_splitk_runs(int M, int N, int K);

@@ -117,7 +117,21 @@ def fold_patch_weight(w: torch.Tensor, channels: int = 3, patch: int = 14, tempo
     return out
 
 
+def quantize_i8(w: torch.Tensor, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Device matrix [rows][cols] (f32 or bf16) -> (int8 codes [rows][cols],
+    float32 row scales [rows]) by qv_quantize_i8."""
+    rows, cols = w.shape
+    q = torch.empty((rows, cols), dtype=torch.int8, device=w.device)
+    sc = torch.empty(rows, dtype=torch.float32, device=w.device)
+    dt = "bf16" if w.dtype == torch.bfloat16 else "f32"
+    check(lib().qv_quantize_i8(_ptr(w), rows, cols, w.stride(0), DTYPES[dt], _ptr(q), _ptr(sc), _stream(stream)))
+    return q, sc
+
+
 # --------------------------------------------------------------------- weights
+WEIGHT_FORMATS = {"dtype": 0, "int8": _abi.QV_I8}
+
+
 @dataclass
 class VisionConfig:
     depth: int
@@ -132,6 +146,7 @@ class VisionConfig:
     rope_theta: float = 1e4
     window: int = 0                 # window side in patches (0: full attention in every block)
     full_blocks: Tuple[int, ...] = ()  # blocks that keep full attention when window > 0
+    weights: str = "dtype"          # block matrices: "dtype" (as the tower) or "int8"
 
     def c(self) -> _abi.VisionCfg:
         mask = 0
@@ -140,7 +155,8 @@ class VisionConfig:
                 raise ValueError(f"full-attention block {b} outside 0..63")
             mask |= 1 << b
         return _abi.VisionCfg(self.depth, self.dim, self.heads, self.mlp, self.patch_dim, self.ld, self.merge,
-                              DTYPES[self.dtype], self.ln_eps, self.rope_theta, self.window, 0, mask)
+                              DTYPES[self.dtype], self.ln_eps, self.rope_theta, self.window,
+                              WEIGHT_FORMATS[self.weights], mask)
 
 
 @dataclass
@@ -166,10 +182,14 @@ def _dev(a: np.ndarray, dtype: str, device, matrix: bool) -> torch.Tensor:
 class VisionWeights:
     """Device copies of the tower parameters and the ctypes struct pointing at
     them.  fold: the Conv3d patch-embed weight is folded on the device into
-    the Conv2d weight of still images (qv_fold_patch_weight)."""
+    the Conv2d weight of still images (qv_fold_patch_weight).  weights="int8":
+    the four block matrices are quantized on the device from their float32
+    values (qv_quantize_i8) and kept only as int8 codes and row scales."""
 
     def __init__(self, params: Dict[str, np.ndarray], depth: int, dtype: str = "bf16", device="cuda",
-                 fold: bool = False):
+                 fold: bool = False, weights: str = "dtype"):
+        if weights not in WEIGHT_FORMATS:
+            raise ValueError(f"weights must be one of {sorted(WEIGHT_FORMATS)}")
         self.tensors: Dict[str, torch.Tensor] = {}
         pw = params["patch_w"]
         self.tensors["patch_w"] = _dev(pw.reshape(pw.shape[0], -1), dtype, device, True)
@@ -182,12 +202,18 @@ class VisionWeights:
             self.patch_b = _dev(params["patch_b"], dtype, device, False)
         blocks = (_abi.BlockW * max(depth, 1))()
         for l in range(depth):
-            vals = []
+            vals, scales = [], {}
             for k in _abi.BLOCK_FIELDS:
                 a = params[f"blocks.{l}.{k}"]
-                t = _dev(a, dtype, device, a.ndim == 2)
+                if weights == "int8" and k in _abi.QUANT_FIELDS:
+                    t, sc = quantize_i8(_dev(a, "f32", device, True))
+                    self.tensors[f"blocks.{l}.{k[:-2]}_s"] = sc
+                    scales[k[:-2] + "_s"] = sc.data_ptr()
+                else:
+                    t = _dev(a, dtype, device, a.ndim == 2)
                 self.tensors[f"blocks.{l}.{k}"] = t
                 vals.append(t.data_ptr())
+            vals += [scales.get(k, 0) for k in _abi.BLOCK_SCALE_FIELDS]
             blocks[l] = _abi.BlockW(*vals)
         self._blocks = blocks
         self.struct = _abi.VisionW(self.tensors["patch_w"].data_ptr(),
@@ -255,7 +281,7 @@ class Encoder:
     def __init__(self, params: Dict[str, np.ndarray], images: Sequence[np.ndarray], depth: int, out_dim: int,
                  dtype: str = "bf16", dim: int = 1280, heads: int = 16, mlp: int = 5120, ln_eps: float = 1e-6,
                  rope_theta: float = 1e4, window: int = 0, full_blocks=(), device="cuda", grids=None,
-                 fold: bool = False, normalize=None, **grid_kw):
+                 fold: bool = False, normalize=None, weights: str = "dtype", **grid_kw):
         self.dtype = dtype
         self.grid_kw = grid_kw
         if grids is None:
@@ -274,9 +300,9 @@ class Encoder:
         pd = patch_width(images[0].shape[1], fold)
         self.vcfg = VisionConfig(depth=depth, dim=dim, heads=heads, mlp=mlp, patch_dim=pd, ld=pd, dtype=dtype,
                                  ln_eps=ln_eps, rope_theta=rope_theta, window=window,
-                                 full_blocks=tuple(full_blocks))
+                                 full_blocks=tuple(full_blocks), weights=weights)
         self.mcfg = MergerConfig(dim=dim, out_dim=out_dim, dtype=dtype, ln_eps=ln_eps)
-        self.vw = VisionWeights(params, depth, dtype, device, fold=fold)
+        self.vw = VisionWeights(params, depth, dtype, device, fold=fold, weights=weights)
         self.mw = MergerWeights(params, dtype, device)
         self.patches = torch.empty((self.n, pd), dtype=TORCH_DTYPES[dtype], device=device)
         self.hidden = torch.empty((self.n, dim), dtype=torch.float32, device=device)

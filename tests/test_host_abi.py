@@ -17,7 +17,7 @@ def test_library_exports_every_header_symbol():
     assert len(names) >= 10
     missing = [n for n in names if not hasattr(L, n)]
     assert not missing, missing
-    assert L.qv_abi_version() == 2
+    assert L.qv_abi_version() == 3
 
 
 def test_grid_params_default():
@@ -95,12 +95,14 @@ def _vcfg(**kw):
     return _abi.VisionCfg(**d)
 
 
-def _vforward(cfg, grids, ws_bytes=1 << 40, null_block=False):
+def _vforward(cfg, grids, ws_bytes=1 << 40, null_block=False, scales=0, **fields):
     L = qv.lib()
     g = np.asarray(grids, np.int32).reshape(-1, 3)
-    blk = _abi.BlockW(*([0x2000] * 12))
+    blk = _abi.BlockW(*([0x2000] * 12 + [scales] * 4))
     if null_block:
         blk.fc2_b = None
+    for k, v in fields.items():
+        setattr(blk, k, v)
     blocks = (_abi.BlockW * 1)(blk)
     w = _abi.VisionW(0x3000, None, blocks)
     return L.qv_vision_forward(ctypes.byref(cfg), ctypes.byref(w), FAKE, g.ctypes.data, len(g), FAKE, FAKE,
@@ -121,7 +123,15 @@ def test_vision_forward_validation():
     assert _vforward(_vcfg(window=3), [(1, 4, 4)]) == _abi.QV_ERR_UNSUPPORTED   # not a multiple of merge
     assert _vforward(_vcfg(window=12), [(1, 4, 4)]) == _abi.QV_ERR_UNSUPPORTED  # more than 100 patches
     assert _vforward(_vcfg(window=-2), [(1, 4, 4)]) == _abi.QV_ERR_UNSUPPORTED
-    assert _vforward(_vcfg(window=8, reserved0=1), [(1, 4, 4)]) == _abi.QV_ERR_SHAPE
+    # int8 block matrices: bf16 tower of width 1280 and MLP 5120 only, scales
+    # required, 16-byte aligned codes
+    I8 = _abi.QV_I8
+    assert _vforward(_vcfg(weights=5), [(1, 4, 4)]) == _abi.QV_ERR_UNSUPPORTED
+    assert _vforward(_vcfg(weights=I8, dtype=_abi.QV_F32), [(1, 4, 4)], scales=0x4000) == _abi.QV_ERR_UNSUPPORTED
+    assert _vforward(_vcfg(weights=I8, mlp=2560), [(1, 4, 4)], scales=0x4000) == _abi.QV_ERR_UNSUPPORTED
+    assert _vforward(_vcfg(weights=I8), [(1, 4, 4)]) == _abi.QV_ERR_NULL            # scales missing
+    assert _vforward(_vcfg(weights=I8), [(1, 4, 4)], scales=0x4000, fc1_w=0x2008) == _abi.QV_ERR_SHAPE
+    assert _vforward(_vcfg(weights=I8), [(1, 4, 4)], scales=0x4000, ws_bytes=1024) == _abi.QV_ERR_WORKSPACE
     n = ctypes.c_size_t()
     g = np.array([[1, 32, 32]], np.int32)
     assert L.qv_vision_workspace_size(ctypes.byref(_vcfg()), g.ctypes.data, 1, ctypes.byref(n)) == 0
@@ -131,6 +141,21 @@ def test_vision_forward_validation():
     nw = ctypes.c_size_t()
     assert L.qv_vision_workspace_size(ctypes.byref(_vcfg(window=2)), g.ctypes.data, 1, ctypes.byref(nw)) == 0
     assert nw.value > n.value
+    # int8 weights at M = 1024: the out-projection and fc2 both leave four
+    # float32 partial sums (4 x 1024 x 1280 x 4 bytes), as fc2 alone does in bf16
+    ni = ctypes.c_size_t()
+    assert L.qv_vision_workspace_size(ctypes.byref(_vcfg(weights=_abi.QV_I8)), g.ctypes.data, 1,
+                                      ctypes.byref(ni)) == 0
+    assert ni.value == n.value
+
+
+def test_quantize_validation():
+    Q = qv.lib().qv_quantize_i8
+    assert Q(None, 4, 16, 16, _abi.QV_F32, FAKE, FAKE, None) == _abi.QV_ERR_NULL
+    assert Q(FAKE, 4, 16, 16, _abi.QV_F32, FAKE, None, None) == _abi.QV_ERR_NULL
+    assert Q(FAKE, 0, 16, 16, _abi.QV_F32, FAKE, FAKE, None) == _abi.QV_ERR_SHAPE
+    assert Q(FAKE, 4, 16, 8, _abi.QV_F32, FAKE, FAKE, None) == _abi.QV_ERR_SHAPE
+    assert Q(FAKE, 4, 16, 16, _abi.QV_I8, FAKE, FAKE, None) == _abi.QV_ERR_UNSUPPORTED
 
 
 def test_patchify_validation():
