@@ -819,6 +819,107 @@ hipError_t gemm_i8w_resid_f32(const void* A, int lda, const int8_t* B, int ldb, 
   }
 }
 
+// Large M: where bf16 uses 256 x 256 tiles (enough of them to fill the
+// GPU), the int8 codes of one matrix are first widened to bf16 in workspace
+// (exact) and multiplied by that kernel; the row scales go onto the float32
+// sums through this wrapper, so the result is the same function as above.
+template <class Inner, class RowMap>
+struct EpiColScale {
+  static constexpr bool kStaged = Inner::kStaged;
+  static constexpr int kPatchFloats = Inner::kPatchFloats;
+  Inner in;
+  const float* scale;
+  RowMap rm;
+  template <int FM, int FN>
+  __device__ __forceinline__ void scale_acc(f32x16 (&acc)[FM][FN], int wn0, int lane, int N) const {
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      const int col = QV_ACC_COL(wn0, fn, lane);
+      const float sc = col < N ? scale[rm(col)] : 0.f;
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[fm][fn][r] *= sc;
+    }
+  }
+  template <int FM, int FN>
+  __device__ __forceinline__ void apply_staged(f32x16 (&acc)[FM][FN], float* wlds, int wm0, int wn0, int lane, int M,
+                                               int N) const {
+    scale_acc(acc, wn0, lane, N);
+    in.apply_staged(acc, wlds, wm0, wn0, lane, M, N);
+  }
+  template <int FM, int FN>
+  __device__ __forceinline__ void apply(f32x16 (&acc)[FM][FN], int wm0, int wn0, int lane, int M, int N) const {
+    scale_acc(acc, wn0, lane, N);
+    in.apply(acc, wm0, wn0, lane, M, N);
+  }
+};
+
+bool gemm_i8w_wide(int M, int N) {
+  return (int64_t)((M + 255) / 256) * ((N + 255) / 256) >= 256;
+}
+
+template <int KT, class Epi, class RowMap>
+static hipError_t launch_i8_wide(const void* A, int lda, const void* codes, int ldb, const float* scale, int M, int N,
+                                 const Epi& epi, RowMap rmap, hipStream_t s) {
+  return launch_pipe<256, 256, 2, 4, 2, KT>(A, lda, codes, ldb, M, N, EpiColScale<Epi, RowMap>{epi, scale, rmap},
+                                            rmap, s);
+}
+
+hipError_t gemm_i8w_wide_qkv(const void* A, int lda, const void* codes, int ldb, const float* scale, int M, int K,
+                             const float* bias, const QkvOut& o, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  if (!A || lda % 8 || ldb % 8 || K != 1280) return hipErrorInvalidValue;
+  return launch_i8_wide<20>(A, lda, codes, ldb, scale, M, 3 * o.dim, EpiQkv{o, bias}, RowMapQkv{o.dim}, s);
+}
+
+hipError_t gemm_i8w_wide_act_bf16(const void* A, int lda, const void* codes, int ldb, const float* scale, int M,
+                                  int N, int K, const float* bias, Act act, void* C, int ldc, hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (!A || lda % 8 || ldb % 8 || N % 32 || K != 1280 || act != Act::QuickGelu) return hipErrorInvalidValue;
+  return launch_i8_wide<20>(A, lda, codes, ldb, scale, M, N, EpiActBf16<Act::QuickGelu>{(uint16_t*)C, ldc, bias},
+                            RowMapIdentity{}, s);
+}
+
+hipError_t gemm_i8w_wide_resid_f32(const void* A, int lda, const void* codes, int ldb, const float* scale, int M,
+                                   int N, int K, const float* bias, float* Z, int ldz, hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (!A || lda % 8 || ldb % 8 || N % 32) return hipErrorInvalidValue;
+  const EpiResidF32 e{Z, ldz, bias};
+  switch (K) {
+    case 1280: return launch_i8_wide<20>(A, lda, codes, ldb, scale, M, N, e, RowMapIdentity{}, s);
+    case 5120: return launch_i8_wide<80>(A, lda, codes, ldb, scale, M, N, e, RowMapIdentity{}, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// int8 codes -> bf16 (exact): 16 codes per thread.
+__global__ __launch_bounds__(256) void k_codes_bf16(const int8_t* __restrict__ q, int64_t n16,
+                                                    uint16_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n16) return;
+  const uint4 w = reinterpret_cast<const uint4*>(q)[i];
+  const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+  uint32_t pk[8];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    pk[2 * d] = pack_bf16_pair((float)(int8_t)wd[d], (float)(int8_t)(wd[d] >> 8));
+    pk[2 * d + 1] = pack_bf16_pair((float)(int8_t)(wd[d] >> 16), (float)((int32_t)wd[d] >> 24));
+  }
+  uint4* o = reinterpret_cast<uint4*>(out) + 2 * i;
+  o[0] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+  o[1] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+}
+
+hipError_t launch_codes_bf16(const int8_t* q, int64_t n, void* out, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (n % 16) return hipErrorInvalidValue;
+  const int64_t n16 = n / 16;
+  QV_KLAUNCH(k_codes_bf16, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, s, q, n16,
+             reinterpret_cast<uint16_t*>(out));
+  return hipGetLastError();
+}
+
 // Symmetric per-row int8: scale = max|w| / 127 (1 for an all-zero row),
 // q = round half to even of w / scale clamped to +-127, all in float32.
 // One 256-thread workgroup per row.

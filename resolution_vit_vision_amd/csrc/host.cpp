@@ -329,6 +329,10 @@ struct VisionPlan {
   int split_fc2 = 1;   // split-K runs of fc2 (bf16, small M)
   int split_proj = 1;  // split-K runs of the out-projection (int8 weights, small M)
   bool i8 = false;     // int8 block matrices
+  // int8 at large M: these products widen their codes to bf16 in off_codes
+  // (one matrix at a time) and use the 256 x 256 bf16 kernel
+  bool wide_qkv = false, wide_proj = false, wide_fc1 = false, wide_fc2 = false;
+  size_t off_codes = 0;
   int window = 0;
   int win_slot = 0;  // padded rows per window: kWinSlot (64) for W <= 8, else kSeqAlign (128)
   int64_t n_win = 0, Pw = 0;
@@ -467,6 +471,19 @@ qv_status make_plan(const qv_vision_cfg* c, const int32_t* grid_thw, int32_t n_i
   vp.off_part = o;
   const int max_split = std::max(vp.split_fc2, vp.split_proj);
   if (max_split > 1) o = align_up(o + (size_t)max_split * N * c->dim * sizeof(float));
+  if (vp.i8 && c->depth > 0) {
+    const int n = (int)N;
+    vp.wide_qkv = gemm_i8w_wide(n, 3 * c->dim);
+    vp.wide_proj = vp.split_proj == 1 && gemm_i8w_wide(n, c->dim);
+    vp.wide_fc1 = gemm_i8w_wide(n, c->mlp);
+    vp.wide_fc2 = vp.split_fc2 == 1 && gemm_i8w_wide(n, c->dim);
+    size_t codes = 0;
+    if (vp.wide_qkv) codes = std::max(codes, (size_t)3 * c->dim * c->dim);
+    if (vp.wide_proj) codes = std::max(codes, (size_t)c->dim * c->dim);
+    if (vp.wide_fc1 || vp.wide_fc2) codes = std::max(codes, (size_t)c->mlp * c->dim);
+    vp.off_codes = o;
+    o = align_up(o + codes * 2);
+  }
   if (vp.window) {
     vp.off_tokw = o;   o = align_up(o + N * sizeof(int2));
     vp.off_outrow = o; o = align_up(o + (size_t)vp.Pw * sizeof(int32_t));
@@ -543,6 +560,7 @@ qv_status qv_vision_forward(const qv_vision_cfg* c, const qv_vision_w* w, const 
   int2* tokw = reinterpret_cast<int2*>(base + vp.off_tokw);
   int32_t* outrow = reinterpret_cast<int32_t*>(base + vp.off_outrow);
   PlanEntry* planw = reinterpret_cast<PlanEntry*>(base + vp.off_planw);
+  void* codes = base + vp.off_codes;
   QkvOut qo{base + vp.off_q, base + vp.off_k, base + vp.off_vt, tok, rope, (int)vp.P, c->dim};
   QkvOut qow{base + vp.off_q, base + vp.off_k, base + vp.off_vt, tokw, rope, (int)vp.Pw, c->dim};
 
@@ -611,7 +629,10 @@ qv_status qv_vision_forward(const qv_vision_cfg* c, const qv_vision_w* w, const 
     qv_status lst = layer_norm(b.ln1_w, b.ln1_b);
     if (lst != QV_OK) return lst;
     if (bf) {
-      if (vp.i8)
+      if (vp.wide_qkv) {
+        QV_LAUNCH(QV_KC_QKV, s, launch_codes_bf16((const int8_t*)b.qkv_w, (int64_t)3 * D * D, codes, s));
+        QV_LAUNCH(QV_KC_QKV, s, gemm_i8w_wide_qkv(A, D, codes, D, b.qkv_s, M, D, (const float*)b.qkv_b, qb, s));
+      } else if (vp.i8)
         QV_LAUNCH(QV_KC_QKV, s, gemm_i8w_qkv(A, D, (const int8_t*)b.qkv_w, D, b.qkv_s, M, D, (const float*)b.qkv_b, qb, s));
       else
         QV_LAUNCH(QV_KC_QKV, s, gemm_bf16_qkv(A, D, b.qkv_w, D, M, D, (const float*)b.qkv_b, qb, s));
@@ -624,6 +645,10 @@ qv_status qv_vision_forward(const qv_vision_cfg* c, const qv_vision_w* w, const 
                                                      part, s));
         pending = vp.split_proj;
         pending_bias = (const float*)b.proj_b;
+      } else if (vp.wide_proj) {
+        QV_LAUNCH(QV_KC_PROJ, s, launch_codes_bf16((const int8_t*)b.proj_w, (int64_t)D * D, codes, s));
+        QV_LAUNCH(QV_KC_PROJ, s, gemm_i8w_wide_resid_f32(O, D, codes, D, b.proj_s, M, D, D, (const float*)b.proj_b,
+                                                         hidden, D, s));
       } else if (vp.i8) {
         QV_LAUNCH(QV_KC_PROJ, s, gemm_i8w_resid_f32(O, D, (const int8_t*)b.proj_w, D, b.proj_s, M, D, D,
                                                     (const float*)b.proj_b, hidden, D, s));
@@ -642,9 +667,19 @@ qv_status qv_vision_forward(const qv_vision_cfg* c, const qv_vision_w* w, const 
     lst = layer_norm(b.ln2_w, b.ln2_b);
     if (lst != QV_OK) return lst;
     if (bf && vp.i8) {
-      QV_LAUNCH(QV_KC_FC1, s, gemm_i8w_act_bf16(A, D, (const int8_t*)b.fc1_w, D, b.fc1_s, M, F, D, (const float*)b.fc1_b,
-                                                Act::QuickGelu, H, F, s));
-      if (vp.split_fc2 > 1) {
+      if (vp.wide_fc1) {
+        QV_LAUNCH(QV_KC_FC1, s, launch_codes_bf16((const int8_t*)b.fc1_w, (int64_t)F * D, codes, s));
+        QV_LAUNCH(QV_KC_FC1, s, gemm_i8w_wide_act_bf16(A, D, codes, D, b.fc1_s, M, F, D, (const float*)b.fc1_b,
+                                                       Act::QuickGelu, H, F, s));
+      } else {
+        QV_LAUNCH(QV_KC_FC1, s, gemm_i8w_act_bf16(A, D, (const int8_t*)b.fc1_w, D, b.fc1_s, M, F, D,
+                                                  (const float*)b.fc1_b, Act::QuickGelu, H, F, s));
+      }
+      if (vp.wide_fc2) {
+        QV_LAUNCH(QV_KC_FC2, s, launch_codes_bf16((const int8_t*)b.fc2_w, (int64_t)D * F, codes, s));
+        QV_LAUNCH(QV_KC_FC2, s, gemm_i8w_wide_resid_f32(H, F, codes, F, b.fc2_s, M, D, F, (const float*)b.fc2_b,
+                                                        hidden, D, s));
+      } else if (vp.split_fc2 > 1) {
         QV_LAUNCH(QV_KC_FC2, s, gemm_i8w_splitk_f32(H, F, (const int8_t*)b.fc2_w, F, b.fc2_s, M, D, F, vp.split_fc2,
                                                     part, s));
         pending = vp.split_fc2;

@@ -144,6 +144,16 @@ hipError_t gemm_i8w_resid_f32(const void* A, int lda, const int8_t* B, int ldb, 
                               int K, const float* bias, float* Z, int ldz, hipStream_t s);
 hipError_t launch_quantize_i8(const void* w, int rows, int cols, int ld, bool bf16, int8_t* q, float* scale,
                               hipStream_t s);
+// Large M (gemm_i8w_wide): codes widened to bf16 by launch_codes_bf16, then
+// the 256 x 256 bf16 kernel with the row scales applied to the sums.
+bool gemm_i8w_wide(int M, int N);
+hipError_t launch_codes_bf16(const int8_t* q, int64_t n, void* out, hipStream_t s);
+hipError_t gemm_i8w_wide_qkv(const void* A, int lda, const void* codes, int ldb, const float* scale, int M, int K,
+                             const float* bias, const QkvOut& o, hipStream_t s);
+hipError_t gemm_i8w_wide_act_bf16(const void* A, int lda, const void* codes, int ldb, const float* scale, int M,
+                                  int N, int K, const float* bias, Act act, void* C, int ldc, hipStream_t s);
+hipError_t gemm_i8w_wide_resid_f32(const void* A, int lda, const void* codes, int ldb, const float* scale, int M,
+                                   int N, int K, const float* bias, float* Z, int ldz, hipStream_t s);
 // Split-K with the reduction left to launch_layernorm_acc: returns the number
 // of K runs that fills the GPU for this shape (1 = no split).
 int gemm_splitk_runs(int M, int N, int K);

@@ -125,6 +125,31 @@ def test_int8_encoder_vs_oracle(name, images, depth, window, full):
     assert e_f > 2 * e_z
 
 
+INT8_WIDE = [
+    # M = 4096: fc1 has enough 256 x 256 tiles for the widened-codes path, the
+    # other products stay on the int8 kernel; M = 13392: all four widened,
+    # ragged last tile
+    ("mixed_4096", [(448, 448, 1)] * 4),
+    ("wide_13392", [(448, 448, 1)] * 13 + [(112, 140, 1)]),
+]
+
+
+@pytest.mark.parametrize("name,images", INT8_WIDE, ids=[c[0] for c in INT8_WIDE])
+def test_int8_large_m_vs_oracle(name, images):
+    grids = [O.grid_thw(h, w, f)[2] for h, w, f in images]
+    _say(f"int8 {name}: {len(images)} images, M = {sum(t * h * w for t, h, w in grids)}, depth 1")
+    wl = synth.small_workload(name, images, depth=1, dtype="bf16")
+    params, imgs = synth.params(wl), synth.pixels(wl)
+    enc = _run(params, imgs, 1)
+    pq = O.dequantized_params(params, 1)
+    z = O.vision_forward(O.patchify(imgs, grids), pq, grids, 1)
+    out = O.patch_merge(z, pq)
+    e_z = rel_l2(enc.hidden.cpu().numpy(), z)
+    e_o = rel_l2(enc.out.float().cpu().numpy(), out)
+    _say(f"  hidden rel-L2 {e_z:.3e}  merged rel-L2 {e_o:.3e}")
+    assert e_z <= TOL and e_o <= TOL
+
+
 def test_int8_codes_on_device_match_oracle():
     """The encoder's device-side codes and scales for every block matrix are
     the oracle's, bit for bit."""
