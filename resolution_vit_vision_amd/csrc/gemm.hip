@@ -725,6 +725,77 @@ hipError_t gemm_bf16_splitk_f32(const void* A, int lda, const void* B, int ldb, 
     default: return hipErrorInvalidValue;
   }
 }
+// Split-K for a product whose output alone leaves most CUs idle (the
+// merger's two Linears at small M): 128 x 160 tiles when N allows, else
+// 128 x 128; the float32 partial sums are reduced by launch_splitk_reduce.
+int gemm_splitk_any_runs(int M, int N, int K) {
+  if (K % 64) return 1;
+  const int kt = K / 64;
+  const int64_t mt = (M + 127) / 128;
+  if (N % 160 == 0) {
+    for (int s : {4, 2})
+      if (kt % s == 0 && mt * (N / 160) * s <= 256 && (kt / s == 20 || kt / s == 40)) return s;
+    return 1;
+  }
+  if (N % 128 == 0) {
+    for (int s : {8, 4, 2})
+      if (kt % s == 0 && mt * (N / 128) * s <= 256 && (kt / s == 10 || kt / s == 20 || kt / s == 40)) return s;
+  }
+  return 1;
+}
+
+hipError_t gemm_bf16_splitk_any_f32(const void* A, int lda, const void* B, int ldb, int M, int N, int K, int splits,
+                                    float* P, hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (N % 160 == 0) return gemm_bf16_splitk_f32(A, lda, B, ldb, M, N, K, splits, P, s);
+  if (splits < 1 || N % 128 || K % 64 || (K / 64) % splits || lda % 8 || ldb % 8) return hipErrorInvalidValue;
+  const EpiPartF32 e{P, N, (size_t)M * N};
+  switch (K / 64 / splits) {
+    case 10: return launch_ws<128, 128, 4, 2, 4, 10, 2>(A, lda, B, ldb, M, N, e, RowMapIdentity{}, s, splits);
+    case 20: return launch_ws<128, 128, 4, 2, 4, 20, 2>(A, lda, B, ldb, M, N, e, RowMapIdentity{}, s, splits);
+    case 40: return launch_ws<128, 128, 4, 2, 4, 40, 2>(A, lda, B, ldb, M, N, e, RowMapIdentity{}, s, splits);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// out[m][n] = bf16(act(sum over runs r = 0, 1, ... of P[r][m][n] + bias[n])),
+// the runs added in index order; four columns per thread.
+template <Act ACT>
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ P, int splits, size_t stride,
+                                                       const float* __restrict__ bias, uint16_t* __restrict__ out,
+                                                       int ldo, int M, int N) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int n4 = N / 4;
+  if (i >= (int64_t)M * n4) return;
+  const int m = (int)(i / n4), c = (int)(i % n4) * 4;
+  const size_t off = (size_t)m * N + c;
+  float4 v = *reinterpret_cast<const float4*>(P + off);
+  for (int r = 1; r < splits; ++r) {
+    const float4 w = *reinterpret_cast<const float4*>(P + r * stride + off);
+    v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+  }
+  const float4 b = *reinterpret_cast<const float4*>(bias + c);
+  uint2 pk;
+  pk.x = pack_bf16(act_apply_fast(ACT, v.x + b.x), act_apply_fast(ACT, v.y + b.y));
+  pk.y = pack_bf16(act_apply_fast(ACT, v.z + b.z), act_apply_fast(ACT, v.w + b.w));
+  *reinterpret_cast<uint2*>(out + (size_t)m * ldo + c) = pk;
+}
+
+hipError_t launch_splitk_reduce(const float* P, int splits, size_t stride, const float* bias, Act act, void* out,
+                                int ldo, int M, int N, hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (N % 4 || ldo % 4 || !bias) return hipErrorInvalidValue;
+  const int64_t n = (int64_t)M * (N / 4);
+  const dim3 grid((unsigned)((n + 255) / 256));
+  uint16_t* o = reinterpret_cast<uint16_t*>(out);
+  switch (act) {
+    case Act::GeluErf: QV_KLAUNCH(k_splitk_reduce<Act::GeluErf>, grid, dim3(256), 0, s, P, splits, stride, bias, o, ldo, M, N); break;
+    case Act::QuickGelu: QV_KLAUNCH(k_splitk_reduce<Act::QuickGelu>, grid, dim3(256), 0, s, P, splits, stride, bias, o, ldo, M, N); break;
+    default: QV_KLAUNCH(k_splitk_reduce<Act::None>, grid, dim3(256), 0, s, P, splits, stride, bias, o, ldo, M, N); break;
+  }
+  return hipGetLastError();
+}
+
 hipError_t gemm_bf16_act_bf16(const void* A, int lda, const void* B, int ldb, int M, int N, int K,
                               const float* bias, Act act, void* C, int ldc, hipStream_t s) {
   uint16_t* c = reinterpret_cast<uint16_t*>(C);

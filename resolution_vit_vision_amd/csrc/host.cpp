@@ -736,7 +736,13 @@ qv_status qv_merge_workspace_size(const qv_merger_cfg* c, int64_t n_tokens, size
   if (st != QV_OK) return st;
   const size_t es = c->dtype == QV_BF16 ? 2 : 4;
   const size_t m = (size_t)n_tokens / (c->merge * c->merge);
-  *bytes = align_up((size_t)n_tokens * c->dim * es) + align_up(m * c->hidden * es);
+  size_t part = 0;  // float32 partial sums of a split-K Linear (bf16, small M)
+  if (c->dtype == QV_BF16) {
+    const int s1 = gemm_splitk_any_runs((int)m, c->hidden, c->hidden);
+    const int s2 = gemm_splitk_any_runs((int)m, c->out_dim, c->hidden);
+    part = std::max(s1 > 1 ? (size_t)s1 * m * c->hidden : 0, s2 > 1 ? (size_t)s2 * m * c->out_dim : 0) * sizeof(float);
+  }
+  *bytes = align_up((size_t)n_tokens * c->dim * es) + align_up(m * c->hidden * es) + align_up(part);
   return QV_OK;
 }
 
@@ -760,9 +766,25 @@ qv_status qv_patch_merge(const qv_merger_cfg* c, const qv_merger_w* w, const flo
   QV_LAUNCH(QV_KC_LAYERNORM, s, launch_layernorm(hidden, (const float*)w->ln_w, (const float*)w->ln_b, Y, bf, (int)n_tokens, c->dim,
                           c->ln_eps, s));
   if (bf) {
-    QV_LAUNCH(QV_KC_MERGE_FC1, s, gemm_bf16_act_bf16(Y, Hd, w->fc1_w, Hd, M, Hd, Hd, (const float*)w->fc1_b, Act::GeluErf, G, Hd, s));
-    QV_LAUNCH(QV_KC_MERGE_FC2, s, gemm_bf16_act_bf16(G, Hd, w->fc2_w, Hd, M, c->out_dim, Hd, (const float*)w->fc2_b, Act::None, out,
-                              c->out_dim, s));
+    // small M: split K so the grid fills the GPU; partials reduced in order
+    float* part = reinterpret_cast<float*>(base + align_up((size_t)n_tokens * c->dim * es) + align_up((size_t)M * Hd * es));
+    const int s1 = gemm_splitk_any_runs(M, Hd, Hd), s2 = gemm_splitk_any_runs(M, c->out_dim, Hd);
+    if (s1 > 1) {
+      QV_LAUNCH(QV_KC_MERGE_FC1, s, gemm_bf16_splitk_any_f32(Y, Hd, w->fc1_w, Hd, M, Hd, Hd, s1, part, s));
+      QV_LAUNCH(QV_KC_MERGE_FC1, s, launch_splitk_reduce(part, s1, (size_t)M * Hd, (const float*)w->fc1_b, Act::GeluErf,
+                                                          G, Hd, M, Hd, s));
+    } else {
+      QV_LAUNCH(QV_KC_MERGE_FC1, s, gemm_bf16_act_bf16(Y, Hd, w->fc1_w, Hd, M, Hd, Hd, (const float*)w->fc1_b, Act::GeluErf,
+                                                        G, Hd, s));
+    }
+    if (s2 > 1) {
+      QV_LAUNCH(QV_KC_MERGE_FC2, s, gemm_bf16_splitk_any_f32(G, Hd, w->fc2_w, Hd, M, c->out_dim, Hd, s2, part, s));
+      QV_LAUNCH(QV_KC_MERGE_FC2, s, launch_splitk_reduce(part, s2, (size_t)M * c->out_dim, (const float*)w->fc2_b,
+                                                          Act::None, out, c->out_dim, M, c->out_dim, s));
+    } else {
+      QV_LAUNCH(QV_KC_MERGE_FC2, s, gemm_bf16_act_bf16(G, Hd, w->fc2_w, Hd, M, c->out_dim, Hd, (const float*)w->fc2_b,
+                                                        Act::None, out, c->out_dim, s));
+    }
   } else {
     QV_LAUNCH(QV_KC_MERGE_FC1, s, gemm_f32_act((const float*)Y, Hd, (const float*)w->fc1_w, Hd, M, Hd, Hd, (const float*)w->fc1_b,
                         Act::GeluErf, (float*)G, Hd, s));

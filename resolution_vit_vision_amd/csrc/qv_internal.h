@@ -157,6 +157,13 @@ hipError_t gemm_i8w_wide_resid_f32(const void* A, int lda, const void* codes, in
 // Split-K with the reduction left to launch_layernorm_acc: returns the number
 // of K runs that fills the GPU for this shape (1 = no split).
 int gemm_splitk_runs(int M, int N, int K);
+// Split-K for the merger's Linears at small M (any N that is a multiple of 128
+// or 160), with the reduction, bias and activation in launch_splitk_reduce.
+int gemm_splitk_any_runs(int M, int N, int K);
+hipError_t gemm_bf16_splitk_any_f32(const void* A, int lda, const void* B, int ldb, int M, int N, int K, int splits,
+                                    float* P, hipStream_t s);
+hipError_t launch_splitk_reduce(const float* P, int splits, size_t stride, const float* bias, Act act, void* out,
+                                int ldo, int M, int N, hipStream_t s);
 // P[s][M][N] = A[:, s K/S .. (s+1) K/S) . B[:, same]^T, float32, no bias.
 hipError_t gemm_bf16_splitk_f32(const void* A, int lda, const void* B, int ldb, int M, int N, int K, int splits,
                                 float* P, hipStream_t s);
