@@ -689,11 +689,20 @@ static hipError_t run_bf16(const void* A, int lda, const void* B, int ldb, int M
 hipError_t gemm_bf16_store_f32(const void* A, int lda, const void* B, int ldb, int M, int N, int K,
                                const float* bias, float* C, int ldc, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
-  constexpr int BM = 128, BN = 128;
-  const unsigned tiles = (unsigned)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
-  QV_KLAUNCH((k_gemm_bf16<BM, BN, 2, 2, EpiStoreF32, RowMapIdentity>), dim3(tiles), dim3(256), 0, s,
-                     reinterpret_cast<const uint16_t*>(A), lda, reinterpret_cast<const uint16_t*>(B), ldb, M, N, K,
-                     EpiStoreF32{C, ldc, bias}, RowMapIdentity{});
+  const EpiStoreF32 e{C, ldc, bias};
+  const uint16_t* a = reinterpret_cast<const uint16_t*>(A);
+  const uint16_t* b = reinterpret_cast<const uint16_t*>(B);
+  const unsigned t128 = (unsigned)(((M + 127) / 128) * ((N + 127) / 128));
+  if (t128 >= 256) {
+    QV_KLAUNCH((k_gemm_bf16<128, 128, 2, 2, EpiStoreF32, RowMapIdentity>), dim3(t128), dim3(256), 0, s, a, lda, b, ldb,
+               M, N, K, e, RowMapIdentity{});
+  } else {
+    // too few 128 x 128 tiles to fill the GPU (the patch embedding of one
+    // 448x448 image has 80): 64 x 64 tiles, several workgroups per CU
+    const unsigned t64 = (unsigned)(((M + 63) / 64) * ((N + 63) / 64));
+    QV_KLAUNCH((k_gemm_bf16<64, 64, 2, 2, EpiStoreF32, RowMapIdentity>), dim3(t64), dim3(256), 0, s, a, lda, b, ldb,
+               M, N, K, e, RowMapIdentity{});
+  }
   return hipGetLastError();
 }
 hipError_t gemm_bf16_resid_f32(const void* A, int lda, const void* B, int ldb, int M, int N, int K,
