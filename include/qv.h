@@ -254,7 +254,9 @@ typedef struct qv_vision_cfg {
 
 /* Bytes of device workspace qv_vision_forward needs for this grid list.
  * grid_thw: host [n_img][3].  Errors: QV_ERR_NULL, QV_ERR_SHAPE,
- * QV_ERR_UNSUPPORTED. */
+ * QV_ERR_UNSUPPORTED (also for a bf16 batch whose widest activation,
+ * N x max(mlp, 3 dim) bf16, reaches 2 GiB: about 209,000 patches at width
+ * 1280; split such a batch over several calls). */
 qv_status qv_vision_workspace_size(const qv_vision_cfg *c, const int32_t *grid_thw,
                                    int32_t n_img, size_t *bytes);
 

@@ -118,8 +118,13 @@ __global__ __launch_bounds__(512) void k_attn_bf16(AttnArgs a, float scale_log2)
   const char* Kt = reinterpret_cast<const char*>(a.k) + kc_offset(head, a.P, pe.prow0, 0) * 2;
   const char* Vh = reinterpret_cast<const char*>(a.vt) + (size_t)head * kHeadDim * a.P * 2;
 
-  // this wave's LDS-DMA blocks of a stage: blocks wave, wave + 8, ...
-  const char* gsrc[LWMAX];
+  // this wave's LDS-DMA blocks of a stage: blocks wave, wave + 8, ..., as
+  // byte offsets from this head's K and V^T (buffer_load ... lds: a FLAT
+  // load that writes LDS would make the compiler wait for every LDS read of
+  // the wave before each MFMA that needs one); the K part of a stage is a
+  // whole number of 1 KB blocks, so each block is all K or all V^T
+  static_assert((K_SLOTS * 16) % 1024 == 0, "K and V^T blocks do not mix");
+  uint32_t goff[LWMAX];
   uint32_t ldst[LWMAX];
 #pragma unroll
   for (int i = 0; i < LWMAX; ++i) {
@@ -127,29 +132,36 @@ __global__ __launch_bounds__(512) void k_attn_bf16(AttnArgs a, float scale_log2)
     blk = blk < BLKS ? blk : BLKS - 1;  // (only used when i < count)
     const int slot = blk * 64 + lane;
     if (slot < K_SLOTS) {
-      gsrc[i] = Kt + (size_t)slot * 16;
+      goff[i] = (uint32_t)slot * 16;
     } else {
       const int sv = slot - K_SLOTS;
       const int d = sv / (IK / 8), p = sv % (IK / 8);
       const int c = v_swz<IK>(d, p);
-      gsrc[i] = Vh + ((size_t)d * a.P + pe.prow0 + 8 * c) * 2;
+      goff[i] = (uint32_t)(((size_t)d * a.P + pe.prow0 + 8 * c) * 2);
     }
     ldst[i] = (uint32_t)(blk * 1024);
   }
   const int nblk = (BLKS - wave + NWV - 1) / NWV;  // blocks this wave issues per stage
+#if defined(__HIP_DEVICE_COMPILE__)
+  const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(Kt), (short)0, 0x7FFFFFFF, 0x00020000);
+  const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(Vh), (short)0, 0x7FFFFFFF, 0x00020000);
 #define QV_ATTN_ISSUE(IT)                                                                                      \
   {                                                                                                            \
     char* stage_ = lds + ((IT) % NST) * STAGE_BYTES;                                                           \
-    const size_t kstep_ = (size_t)(IT) * IK * 160; /* K: IK keys x 160 B, contiguous */                       \
-    const size_t vstep_ = (size_t)(IT) * IK * 2;   /* V^T: IK keys along each row */                          \
     _Pragma("unroll") for (int i = 0; i < LWMAX; ++i) {                                                        \
       if (i < nblk) {                                                                                          \
-        const bool isk_ = (int)ldst[i] < K_SLOTS * 16;                                                         \
-        __builtin_amdgcn_global_load_lds((gas_ptr)(gsrc[i] + (isk_ ? kstep_ : vstep_)),                       \
-                                         (las_ptr)(stage_ + ldst[i]), 16, 0, 0);                               \
+        if ((int)ldst[i] < K_SLOTS * 16) /* K: IK keys x 160 B per stage, contiguous */                       \
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (las_ptr)(stage_ + ldst[i]), 16, goff[i],               \
+                                                   (IT) * IK * 160, 0, 0);                                     \
+        else /* V^T: IK keys along each row */                                                                 \
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (las_ptr)(stage_ + ldst[i]), 16, goff[i],               \
+                                                   (IT) * IK * 2, 0, 0);                                       \
       }                                                                                                        \
     }                                                                                                          \
   }
+#else
+#define QV_ATTN_ISSUE(IT) {}
+#endif
 
 
   f32x16 o[3];
@@ -381,8 +393,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
   const char* Kt = reinterpret_cast<const char*>(a.k) + kc_offset(head, a.P, pe.prow0, 0) * 2;
   const char* Vh = reinterpret_cast<const char*>(a.vt) + (size_t)head * kHeadDim * a.P * 2;
 
-  // DMA sources of this wave's blocks (block wave + NW i of each stage)
-  const char* gsrc[LWMAX];
+  // DMA sources of this wave's blocks (block wave + NW i of each stage), as
+  // byte offsets from this head's K and V^T (buffer_load ... lds: a FLAT
+  // load that writes LDS would make the compiler wait for every LDS read of
+  // the wave before each MFMA that needs one).  K_BYTES is a whole number
+  // of 1 KB blocks, so each block is all K or all V^T.
+  static_assert(K_BYTES % 1024 == 0, "K and V^T blocks do not mix");
+  uint32_t goff[LWMAX];
   int ldst[LWMAX];
   bool isk[LWMAX];
 #pragma unroll
@@ -391,28 +408,37 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
     blk = blk < BLKS ? blk : BLKS - 1;
     const int slot = blk * 64 + lane;
     if (slot < K_BYTES / 16) {
-      gsrc[i] = Kt + (size_t)slot * 16;
+      goff[i] = (uint32_t)slot * 16;
       isk[i] = true;
     } else {
       const int sv = slot - K_BYTES / 16;
       const int d = sv >> 2, p = sv & 3;
       const int c = p ^ ((d >> 2) & 3);
-      gsrc[i] = Vh + ((size_t)d * a.P + pe.prow0 + 8 * c) * 2;
+      goff[i] = (uint32_t)(((size_t)d * a.P + pe.prow0 + 8 * c) * 2);
       isk[i] = false;
     }
     ldst[i] = blk * 1024;
   }
   const int nblk = (BLKS - wave + NW - 1) / NW;
+#if defined(__HIP_DEVICE_COMPILE__)
+  const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(Kt), (short)0, 0x7FFFFFFF, 0x00020000);
+  const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(Vh), (short)0, 0x7FFFFFFF, 0x00020000);
 #define QV_L_ISSUE(IT, ST)                                                                                   \
   {                                                                                                          \
     _Pragma("unroll") for (int i = 0; i < LWMAX; ++i) {                                                      \
       if (i < nblk) {                                                                                        \
-        const size_t step_ = isk[i] ? (size_t)(IT) * K_BYTES : (size_t)(IT) * IK * 2;                       \
-        __builtin_amdgcn_global_load_lds((gas_ptr)(gsrc[i] + step_), (las_ptr)(lds + (ST) * STRIDE + ldst[i]), \
-                                         16, 0, 0);                                                          \
+        if (isk[i])                                                                                          \
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (las_ptr)(lds + (ST) * STRIDE + ldst[i]), 16, goff[i],  \
+                                                   (IT) * K_BYTES, 0, 0);                                    \
+        else                                                                                                 \
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (las_ptr)(lds + (ST) * STRIDE + ldst[i]), 16, goff[i],  \
+                                                   (IT) * IK * 2, 0, 0);                                     \
       }                                                                                                      \
     }                                                                                                        \
   }
+#else
+#define QV_L_ISSUE(IT, ST) {}
+#endif
 
   // per-lane LDS offsets (stage offsets are immediates)
   const int koff = (hlf * 32 + l32) * 16;
@@ -636,20 +662,25 @@ __global__ __launch_bounds__(128) void k_attn_win(AttnArgs a, float scale_log2) 
 
   const char* Kt = reinterpret_cast<const char*>(a.k) + kc_offset(head, a.P, pe.prow0, 0) * 2;
   const char* Vh = reinterpret_cast<const char*>(a.vt) + ((size_t)head * kHeadDim * a.P + pe.prow0) * 2;
+  // buffer_load ... lds, as in the kernels above (K_BYTES is whole blocks)
+  static_assert(K_BYTES % 1024 == 0, "K and V^T blocks do not mix");
+#if defined(__HIP_DEVICE_COMPILE__)
+  const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(Kt), (short)0, 0x7FFFFFFF, 0x00020000);
+  const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(Vh), (short)0, 0x7FFFFFFF, 0x00020000);
 #pragma unroll
   for (int i = 0; i < BLKS / 2; ++i) {
     const int blk = wave + 2 * i;
     const int slot = blk * 64 + lane;  // 16-byte slot of the LDS image
-    const char* src;
     if (slot < K_BYTES / 16) {
-      src = Kt + (size_t)slot * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (las_ptr)(lds + blk * 1024), 16, (uint32_t)slot * 16, 0, 0, 0);
     } else {
       const int sv = slot - K_BYTES / 16;
       const int d = sv >> 3, p = sv & 7;
-      src = Vh + ((size_t)d * a.P + 8 * (p ^ ((d >> 1) & 7))) * 2;
+      const uint32_t off = (uint32_t)(((size_t)d * a.P + 8 * (p ^ ((d >> 1) & 7))) * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (las_ptr)(lds + blk * 1024), 16, off, 0, 0, 0);
     }
-    __builtin_amdgcn_global_load_lds((gas_ptr)src, (las_ptr)(lds + blk * 1024), 16, 0, 0);
   }
+#endif
   const int q0 = 32 * wave;
   bf16x8 qf[5];
   {

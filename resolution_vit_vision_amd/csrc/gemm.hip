@@ -624,6 +624,8 @@ static XcdCut xcd_cut(int tiles_m, int tiles_n, int BM, int BN) {
 template <int BM, int BN, int WM, int WN, int ST, int KT, int KS = 1, class Epi, class RowMap>
 static hipError_t launch_pipe(const void* A, int lda, const void* B, int ldb, int M, int N, const Epi& epi,
                               RowMap rmap, hipStream_t s) {
+  // the kernel addresses its operands with 32-bit byte offsets below 2 GiB
+  if ((size_t)M * lda * 2 >= 0x7FFFFFFFu || (size_t)N * ldb * 2 >= 0x7FFFFFFFu) return hipErrorInvalidValue;
   const XcdCut cut = xcd_cut((M + BM - 1) / BM, (N + BN - 1) / BN, BM, BN);
   QV_KLAUNCH((k_gemm_pipe<BM, BN, WM, WN, ST, KT / KS, KS, Epi, RowMap>), dim3(cut.grid), dim3(WM * WN * KS * 64),
                      0, s, reinterpret_cast<const uint16_t*>(A), lda, reinterpret_cast<const uint16_t*>(B), ldb, M, N,

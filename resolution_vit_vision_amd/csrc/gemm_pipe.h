@@ -65,10 +65,20 @@ struct PipeCfg {
   static_assert(KS_ == 1 || KS_ == 2, "K split 1 or 2");
 };
 
+// The loads are buffer_load ... lds (MUBUF) rather than global_load_lds:
+// the compiler counts a FLAT instruction that writes LDS as both a memory
+// and an LDS access, and while one is in flight it waits for every LDS read
+// of the wave (lgkmcnt(0)) before the first MFMA of a step; with the buffer
+// form the waits name only the fragments each MFMA needs.  Offsets are
+// 32-bit bytes from each matrix's base (every operand is below 2 GiB; the
+// host checks).
 template <class C>
 struct PipeState {
-  const char* gsrc[C::LOADS];   // per-thread global address of its chunk at step 0
+  uint32_t voff[C::LOADS];      // byte offset of this thread's chunk at step 0 from its matrix's base
   uint32_t ldst[C::LOADS];      // wave-uniform LDS byte offset of the 1 KB block inside a stage
+  uint32_t amask;               // bit i: load i reads A (wave-uniform)
+  const void* abase;
+  const void* bbase;
 };
 
 template <class C, class RowMap>
@@ -88,22 +98,38 @@ __device__ __forceinline__ void pipe_setup(PipeState<C>& ps, const uint16_t* A, 
     if (isA) {
       int g = m0 + r;
       g = g < M ? g : M - 1;
-      ps.gsrc[i] = reinterpret_cast<const char*>(A + (size_t)g * lda + ks * 64 + c * 8);
+      ps.voff[i] = (uint32_t)(((size_t)g * lda + ks * 64 + c * 8) * 2);
     } else {
       int g = n0 + r;
       g = g < N ? g : N - 1;
-      ps.gsrc[i] = reinterpret_cast<const char*>(B + (size_t)rmap(g) * ldb + ks * 64 + c * 8);
+      ps.voff[i] = (uint32_t)(((size_t)rmap(g) * ldb + ks * 64 + c * 8) * 2);
     }
     ps.ldst[i] = (uint32_t)(blk * 1024);
   }
+  uint32_t am = 0;
+#pragma unroll
+  for (int i = 0; i < C::LOADS; ++i)
+    if ((((i * C::NW + wave) * 64) % ((C::BM + C::BN) * 8)) < C::BM * 8) am |= 1u << i;
+  ps.amask = am;
+  ps.abase = A;
+  ps.bbase = B;
 }
 
 template <class C>
 __device__ __forceinline__ void pipe_issue(const PipeState<C>& ps, uint16_t* stage, int kt) {
+  // device pass only: the buffer-resource type exists for the GPU target alone
+#if defined(__HIP_DEVICE_COMPILE__)
+  const auto ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(ps.abase), (short)0, 0x7FFFFFFF, 0x00020000);
+  const auto rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(ps.bbase), (short)0, 0x7FFFFFFF, 0x00020000);
 #pragma unroll
-  for (int i = 0; i < C::LOADS; ++i)
-    __builtin_amdgcn_global_load_lds((gas_ptr)(ps.gsrc[i] + (size_t)kt * 128 * C::KS),
-                                     (las_ptr)(reinterpret_cast<char*>(stage) + ps.ldst[i]), 16, 0, 0);
+  for (int i = 0; i < C::LOADS; ++i) {
+    char* dst = reinterpret_cast<char*>(stage) + ps.ldst[i];
+    if ((ps.amask >> i) & 1u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (las_ptr)dst, 16, ps.voff[i], kt * 128 * C::KS, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (las_ptr)dst, 16, ps.voff[i], kt * 128 * C::KS, 0, 0);
+  }
+#endif
 }
 
 // Operand fragments are software-pipelined: the LDS reads of k-step kk + 1

@@ -390,6 +390,10 @@ qv_status make_plan(const qv_vision_cfg* c, const int32_t* grid_thw, int32_t n_i
   }
   vp.P = prow;
   if (vp.P > INT32_MAX / 2) return fail(QV_ERR_SHAPE, "batch too large");
+  // bf16 matrix products address operands with 32-bit byte offsets: the
+  // widest activation ([N][mlp] or [N][3 dim] bf16) must stay below 2 GiB
+  if (c->dtype == QV_BF16 && (size_t)vp.N * std::max(c->mlp, 3 * c->dim) * 2 >= 0x7FFFFFFFu)
+    return fail(QV_ERR_UNSUPPORTED, "batch of %lld patches too large for one call", (long long)vp.N);
   int64_t tiles128 = 0;
   for (int i = 0; i < n_img; ++i) tiles128 += (vp.desc[i].n + 127) / 128;
   vp.attn_rows = c->dtype == QV_BF16 ? attention_bf16_rows_per_wg(tiles128 * c->heads) : kAttnBQ_f32;

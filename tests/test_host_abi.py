@@ -147,6 +147,15 @@ def test_vision_forward_validation():
     assert L.qv_vision_workspace_size(ctypes.byref(_vcfg(weights=_abi.QV_I8)), g.ctypes.data, 1,
                                       ctypes.byref(ni)) == 0
     assert ni.value == n.value
+    # a bf16 batch whose [N][mlp] activation would reach 2 GiB is refused up
+    # front (512 x 512 patches: 262,144 x 5120 x 2 bytes); f32 mode is not
+    # limited this way
+    big = np.array([[1, 512, 512]], np.int32)
+    assert L.qv_vision_workspace_size(ctypes.byref(_vcfg()), big.ctypes.data, 1, ctypes.byref(nw)) == \
+        _abi.QV_ERR_UNSUPPORTED
+    assert _vforward(_vcfg(), [(1, 512, 512)]) == _abi.QV_ERR_UNSUPPORTED
+    assert L.qv_vision_workspace_size(ctypes.byref(_vcfg(dtype=_abi.QV_F32)), big.ctypes.data, 1,
+                                      ctypes.byref(nw)) == 0
 
 
 def test_quantize_validation():
