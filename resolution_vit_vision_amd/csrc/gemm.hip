@@ -660,7 +660,11 @@ static hipError_t run_pipe(const void* A, int lda, const void* B, int ldb, int M
   const int64_t t256 = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
   const int64_t t128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
   const int64_t t160 = (int64_t)((M + 127) / 128) * (N / 160);
-  if (t256 >= 256) return launch_pipe<256, 256, 2, 4, 2, KT>(A, lda, B, ldb, M, N, epi, rmap, s);
+  // 256 x 256 tiles keep the matrix pipes ~47 % busy against ~32 % for the
+  // 128 x 128 warp-specialized kernel at these sizes, so one round of them
+  // on 160 or more CUs beats about three rounds of the smaller tile
+  // (4 x 672x672: fc2 5.25 -> 4.24 ms per forward at 180 tiles)
+  if (t256 >= 160) return launch_pipe<256, 256, 2, 4, 2, KT>(A, lda, B, ldb, M, N, epi, rmap, s);
   if constexpr (ALLOW160)
     if (N % 160 == 0 && t160 >= 192 && t160 <= 256)
       return launch_ws<128, 160, 4, 1, 4, KT, 4>(A, lda, B, ldb, M, N, epi, rmap, s);
@@ -938,7 +942,7 @@ struct EpiColScale {
 };
 
 bool gemm_i8w_wide(int M, int N) {
-  return (int64_t)((M + 255) / 256) * ((N + 255) / 256) >= 256;
+  return (int64_t)((M + 255) / 256) * ((N + 255) / 256) >= 160;  // the bf16 rule in run_pipe
 }
 
 template <int KT, class Epi, class RowMap>

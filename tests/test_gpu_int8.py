@@ -126,9 +126,9 @@ def test_int8_encoder_vs_oracle(name, images, depth, window, full):
 
 
 INT8_WIDE = [
-    # M = 4096: fc1 has enough 256 x 256 tiles for the widened-codes path, the
-    # other products stay on the int8 kernel; M = 13392: all four widened,
-    # ragged last tile
+    # M = 4096: fc1 and q/k/v have enough 256 x 256 tiles for the
+    # widened-codes path, the out-projection and fc2 stay on the int8 kernel;
+    # M = 13392: all four widened, ragged last tile
     ("mixed_4096", [(448, 448, 1)] * 4),
     ("wide_13392", [(448, 448, 1)] * 13 + [(112, 140, 1)]),
 ]
