@@ -1,9 +1,10 @@
 // Multi-stage C = A . B^T for gfx950 with direct global->LDS loads.
 //
 // Each stage holds a BM x 64 tile of A and a BN x 64 tile of B (bf16, row =
-// 128 bytes of 8 16-byte chunks).  Tiles are fetched with
-// global_load_lds_dwordx4: one instruction moves 64 lanes x 16 bytes into 1 KB
-// of LDS at the wave-uniform base (lane l lands at base + 16 l), so the LDS
+// 128 bytes of 8 16-byte chunks).  Tiles are fetched by LDS-DMA
+// (buffer_load_dwordx4 ... lds, or global_load_lds_dwordx4 in waves that
+// never read LDS): one instruction moves 64 lanes x 16 bytes into 1 KB of
+// LDS at the wave-uniform base (lane l lands at base + 16 l), so the LDS
 // layout is chosen by which global chunk each lane fetches.  The layout is
 // row-major with the chunk index XOR-ed by (row >> 1) & 7: the operand reads
 // of v_mfma_f32_32x32x16_bf16 (32 consecutive rows, one 16-byte chunk per
