@@ -208,24 +208,28 @@ def _sampled_rows(cu, rng, per_image=4):
     return np.unique(np.asarray(rows))
 
 
-FULL = ["qwen2vl_2b_672x4_varlen", "mixed16_varlen_7b_merger", "maxres_3584", "qwen25vl_7b_3584_window",
-        "video_448_16f"]
+FULL = [(n, "dtype") for n in ("qwen2vl_2b_672x4_varlen", "mixed16_varlen_7b_merger", "maxres_3584",
+                                "qwen25vl_7b_3584_window", "video_448_16f")]
+# int8 block matrices at full size (bench --weights int8): the blocks are
+# checked against the oracle on the dequantized weights
+FULL += [("qwen2vl_2b_672x4_varlen", "int8"), ("qwen25vl_7b_3584_window", "int8")]
 
 
-@pytest.mark.parametrize("name", FULL)
-def test_full_size_sampled(name):
+@pytest.mark.parametrize("name,weights", FULL, ids=[n if w == "dtype" else f"{n}-int8" for n, w in FULL])
+def test_full_size_sampled(name, weights):
     """Full-size workload in the benchmark's launch configuration (still
     images take the Conv2d fold there): exact patchify and metadata; first
     and last block teacher-forced on sampled rows; merger on sampled groups."""
     qv = _qv()
     wl = synth.WORKLOADS[name]
-    _say(f"{name}: drawing inputs")
+    _say(f"{name} weights={weights}: drawing inputs")
     params = synth.params(wl)
     imgs = synth.pixels(wl)
     grids = [O.grid_thw(h, w, f)[2] for h, w, f in wl.images]
     fold = all(f == 1 for _, _, f in wl.images)
     enc = qv.Encoder(params, imgs, depth=wl.depth, out_dim=wl.out_dim, dtype=wl.dtype, window=wl.window,
-                     full_blocks=wl.full_blocks, fold=fold)
+                     full_blocks=wl.full_blocks, fold=fold, weights=weights)
+    block_ref = O.dequantized_params(params, wl.depth) if weights == "int8" else params
     assert enc.grids == [tuple(g) for g in grids]
     cu, pos, _ = O.seq_meta(grids)
     windows = O.window_groups(grids, wl.window) if wl.window else None
@@ -249,7 +253,7 @@ def test_full_size_sampled(name):
         torch.cuda.synchronize()
         groups = windows if (windows is not None and l not in wl.full_blocks) else None
         _say(f"{name}: block {l} ({'windowed' if groups else 'full'}) teacher-forced on {len(rows)} rows")
-        ref = O.vision_block_rows(z_in, O.block_params(params, l), cu, angles, rows, groups=groups)
+        ref = O.vision_block_rows(z_in, O.block_params(block_ref, l), cu, angles, rows, groups=groups)
         e = rel_l2(z_out[rows], ref)
         _say(f"  block {l} rel-L2 {e:.3e}")
         assert e <= wl.tol
