@@ -97,14 +97,18 @@ def cpu_baseline(wl, params, imgs):
     except Exception:  # pragma: no cover
         blas_threads = None
     cores = len(os.sched_getaffinity(0))
-    t0 = time.perf_counter()
-    grids, z, out = O.encode(imgs, params, depth=wl.depth, window=wl.window, full_blocks=wl.full_blocks)
-    dt = time.perf_counter() - t0
+    # whole passes over the workload until at least 10 s of CPU time (at most 4)
+    passes, dt = 0, 0.0
+    while passes < 4 and (passes == 0 or dt < 10.0):
+        t0 = time.perf_counter()
+        grids, z, out = O.encode(imgs, params, depth=wl.depth, window=wl.window, full_blocks=wl.full_blocks)
+        dt += time.perf_counter() - t0
+        passes += 1
     m = out.shape[0]
-    return {"value": m / dt, "unit": "tokens/s", "cores": max(cores, blas_threads or 1), "kind": "oracle",
+    return {"value": m * passes / dt, "unit": "tokens/s", "cores": max(cores, blas_threads or 1), "kind": "oracle",
             "sample": f"whole workload ({wl.name}: {len(imgs)} image(s), {m} merged tokens, {wl.depth} blocks), "
-                      f"float64 numpy, one pass, {dt:.1f} s",
-            "seconds": dt, "blas_threads": blas_threads, "affinity_cores": cores}
+                      f"float64 numpy, {passes} pass(es) in {dt:.1f} s",
+            "seconds": dt, "passes": passes, "blas_threads": blas_threads, "affinity_cores": cores}
 
 
 def copy_calibration():
