@@ -40,6 +40,11 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 // instead of every key block, and P stays <= 2^kLazyLog2 (safe in bf16/f32).
 constexpr float kLazyLog2 = 8.0f;
 
+// Maximum of two scores.  IEEE maximum (NaN-propagating) needs no quieting of
+// its inputs, unlike fmaxf, so a max of three costs one v_maximum3_f32; the
+// scores are never NaN, so the result equals fmaxf's.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 __device__ __forceinline__ int find_plan(const PlanEntry* plan, int n_img, int gt) {
   int lo = 0, hi = n_img - 1;
   while (lo < hi) {
@@ -236,8 +241,8 @@ __global__ __launch_bounds__(512) void k_attn_bf16(AttnArgs a, float scale_log2)
     QV_ATTN_MASK(it, s_cur)
     float mx = s_cur[0];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s_cur[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    for (int r = 1; r < 16; ++r) mx = vmax(mx, s_cur[r]);
+    mx = vmax(mx, __shfl_xor(mx, 32, 64));
     const float cand = mx * scale_log2;
     const bool grow = cand > m_run + kLazyLog2;
     if (__any(grow)) {
@@ -344,13 +349,17 @@ __global__ __launch_bounds__(512) void k_attn_bf16(AttnArgs a, float scale_log2)
 // NW = 4 waves of 32 queries, keys streamed 32 per stage through a 4-stage
 // LDS-DMA ring (K tile 5 KB + V^T 5 KB + a 32-byte constant block holding the
 // ones row, per stage), the stage index a compile-time constant of a loop
-// unrolled by 4 so every LDS address is an immediate offset.  Per step the
-// scores of the next tile are formed while the current tile's exponentials
-// run (sched_group_barrier interleaves the 5 MFMAs with the VALU work), then
-// the running max of the next tile is taken while its P.V MFMAs run.  V^T
-// chunks are XOR-swizzled by (row >> 2) & 3 (64-byte rows): the 16 rows one
-// pass of a 16-byte read touches cover all 64 banks.  Measured against the
-// 8-wave kernel at n = 9216 .. 65,536: +7-11 % (1.0-1.07 PFLOP/s).
+// unrolled by 4 so every LDS address is an immediate offset.  The VALU work
+// of a step (16 exponentials, 8 bf16 packs, the next tile's max) is spread
+// over its 11 MFMAs with sched_group_barrier: the first 8 exponentials of
+// the current tile run beside the 5 score MFMAs of the next tile, the other
+// 8 beside the P.V MFMAs of the first 16 keys, the max of the next tile
+// beside those of the last 16 keys (2.4 % faster at n = 16,384 and 65,536
+// than all 16 exponentials beside the score MFMAs, together with the
+// quieting-free max).  V^T chunks are XOR-swizzled by (row >> 2) & 3 (64-byte
+// rows): the 16 rows one pass of a 16-byte read touches cover all 64 banks.
+// Measured against the 8-wave kernel at n = 9216 .. 65,536: +9-14 %
+// (1.06-1.13 PFLOP/s).
 // The occupancy request of 4 waves per SIMD is not met (168 VGPRs leave 3),
 // but the schedule the compiler builds under it measured 8-10 % faster than
 // with no request or a request of 3; the unmet-target warning is silenced.
@@ -492,10 +501,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
   }
 #define QV_L_MAX(SACC, OUT)                                                                                  \
   {                                                                                                          \
-    float m_ = fmaxf(fmaxf(SACC[0], SACC[1]), SACC[2]);                                                     \
-    _Pragma("unroll") for (int r = 3; r < 16; r += 2) m_ = fmaxf(fmaxf(m_, SACC[r]), SACC[r + 1 < 16 ? r + 1 : r]); \
-    const auto sw_ = __builtin_amdgcn_permlane32_swap(__float_as_uint(m_), __float_as_uint(m_), false, false); \
-    OUT = fmaxf(__uint_as_float(sw_[0]), __uint_as_float(sw_[1]));                             \
+    float m_ = vmax(vmax(SACC[0], SACC[1]), SACC[2]);                                                        \
+    _Pragma("unroll") for (int r = 3; r < 16; r += 2) m_ = vmax(vmax(m_, SACC[r]), SACC[r + 1 < 16 ? r + 1 : r]);\
+    const auto sw_ = __builtin_amdgcn_permlane32_swap(__float_as_uint(m_), __float_as_uint(m_), false, false);\
+    OUT = vmax(__uint_as_float(sw_[0]), __uint_as_float(sw_[1]));                                            \
   }
 
   // q arrives pre-scaled by log2(e)/sqrt(80) (the q/k/v epilogue), so the
@@ -533,36 +542,43 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
     _Pragma("unroll") for (int kk = 1; kk < 5; ++kk)                                                        \
       s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf_[kk], qf[kk], s_nxt, 0, 0, 0);                      \
     bf16x8 pb[2];                                                                                            \
-    _Pragma("unroll") for (int s2 = 0; s2 < 2; ++s2)                                                        \
-    _Pragma("unroll") for (int e = 0; e < 8; ++e)                                                           \
-      pb[s2][e] = (__bf16)__builtin_amdgcn_exp2f(s_cur[8 * s2 + e]);                                          \
+    _Pragma("unroll") for (int e = 0; e < 8; ++e)                                                            \
+      pb[0][e] = (__bf16)__builtin_amdgcn_exp2f(s_cur[e]);                                                   \
     bf16x8 vf_[6];                                                                                           \
-    _Pragma("unroll") for (int s2 = 0; s2 < 2; ++s2)                                                        \
-    _Pragma("unroll") for (int t = 0; t < 3; ++t)                                                           \
+    _Pragma("unroll") for (int s2 = 0; s2 < 2; ++s2)                                                         \
+    _Pragma("unroll") for (int t = 0; t < 3; ++t)                                                            \
       vf_[3 * s2 + t] = *reinterpret_cast<const bf16x8*>(lds + (ST) * STRIDE +                               \
-                                                       (t < 2 ? voff[s2] + t * 2048 : voff2[s2]));          \
-    asm volatile("" ::"v"(pb[0]), "v"(pb[1]));                                                              \
+                                                       (t < 2 ? voff[s2] + t * 2048 : voff2[s2]));           \
+    asm volatile("" ::"v"(pb[0]));                                                                           \
     {                                                                                                        \
       __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);                                                     \
-      __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);                                                     \
-      _Pragma("unroll") for (int g_ = 0; g_ < 4; ++g_) {                                                    \
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                   \
-        __builtin_amdgcn_sched_group_barrier(0x402, 7, 0);                                                   \
-      }                                                                                                      \
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                     \
-      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);                                                     \
-      __builtin_amdgcn_sched_group_barrier(0x402, 12, 0);                                                    \
-    }                                                                                                        \
-    if (more_) QV_L_MASK((IT) + 1, s_nxt)                                                                    \
-    float cand_;                                                                                             \
-    QV_L_MAX(s_nxt, cand_)                                                                                   \
-    _Pragma("unroll") for (int s2 = 0; s2 < 2; ++s2)                                                        \
-    _Pragma("unroll") for (int t = 0; t < 3; ++t)                                                           \
-      o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf_[3 * s2 + t], pb[s2], o[t], 0, 0, 0);               \
-    {                                                                                                        \
-      _Pragma("unroll") for (int g_ = 0; g_ < 6; ++g_) {                                                    \
+      __builtin_amdgcn_sched_group_barrier(0x402, 3, 0);                                                     \
+      _Pragma("unroll") for (int g_ = 0; g_ < 3; ++g_) {                                                     \
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                   \
         __builtin_amdgcn_sched_group_barrier(0x402, 3, 0);                                                   \
+      }                                                                                                      \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                     \
+      __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);                                                     \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                     \
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);                                                     \
+    }                                                                                                        \
+    if (more_) QV_L_MASK((IT) + 1, s_nxt)                                                                    \
+    _Pragma("unroll") for (int t = 0; t < 3; ++t)                                                            \
+      o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf_[t], pb[0], o[t], 0, 0, 0);                          \
+    _Pragma("unroll") for (int e = 0; e < 8; ++e)                                                            \
+      pb[1][e] = (__bf16)__builtin_amdgcn_exp2f(s_cur[8 + e]);                                               \
+    float cand_;                                                                                             \
+    QV_L_MAX(s_nxt, cand_)                                                                                   \
+    _Pragma("unroll") for (int t = 0; t < 3; ++t)                                                            \
+      o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf_[3 + t], pb[1], o[t], 0, 0, 0);                      \
+    {                                                                                                        \
+      _Pragma("unroll") for (int g_ = 0; g_ < 3; ++g_) {                                                     \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                   \
+        __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);                                                   \
+      }                                                                                                      \
+      _Pragma("unroll") for (int g_ = 0; g_ < 3; ++g_) {                                                     \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                   \
+        __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);                                                   \
       }                                                                                                      \
     }                                                                                                        \
     const bool grow_ = more_ && cand_ > kLazyLog2;                                                           \
@@ -711,9 +727,9 @@ __global__ __launch_bounds__(128) void k_attn_win(AttnArgs a, float scale_log2) 
     for (int r = 0; r < 16; ++r) {
       const int key = 32 * t + 8 * (r >> 2) + 4 * hlf + (r & 3);
       if (key >= n) sc[t][r] = -INFINITY;
-      mx = fmaxf(mx, sc[t][r]);
+      mx = vmax(mx, sc[t][r]);
     }
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  mx = vmax(mx, __shfl_xor(mx, 32, 64));
   const float msc = mx * scale_log2;  // key 0 is always valid: mx is finite
   bf16x8 pb[2][2];
 #pragma unroll
