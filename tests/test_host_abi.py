@@ -217,3 +217,22 @@ def test_merge_validation():
     assert L.qv_patch_merge(*args(16, 16)) == _abi.QV_ERR_WORKSPACE
     c.hidden = 5000
     assert L.qv_patch_merge(*args(16, 1 << 40)) == _abi.QV_ERR_SHAPE
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    """No CPU fallback: without libqv.so the package refuses to run."""
+    monkeypatch.setattr(_abi, "LIB_PATH", "/nonexistent/libqv.so")
+    monkeypatch.setattr(_abi, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        _abi.lib()
+
+
+def test_encoder_without_gpu_raises():
+    """On a host with no GPU the encoder raises instead of computing on the CPU."""
+    import torch
+    import synth
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    wl = synth.small_workload("nogpu", [(56, 56, 1)], depth=1, dtype="bf16")
+    with pytest.raises(RuntimeError, match="GPU"):
+        qv.Encoder(synth.params(wl), synth.pixels(wl), depth=1, out_dim=1536, dtype="bf16")
