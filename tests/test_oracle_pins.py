@@ -425,6 +425,155 @@ def test_block_rows_equals_block_windowed():
     assert not np.allclose(O.vision_block_rows(z, p, cu, a, rows), full[rows])
 
 
+def _both_block_forms(z, p, cu, angles, **kw):
+    """The block through vision_block (whole) and vision_block_rows (every row,
+    and a scattered subset), so a wiring pin holds for both forms."""
+    full = O.vision_block(z, p, cu, angles, **kw)
+    n = z.shape[0]
+    sub = np.arange(0, n, 3)
+    return [(np.arange(n), full),
+            (np.arange(n), O.vision_block_rows(z, p, cu, angles, np.arange(n), **kw)),
+            (sub, O.vision_block_rows(z, p, cu, angles, sub, **kw))]
+
+
+# QuickGELU u * sigmoid(1.702 u) at u = -2, -1, -0.5, 0, 0.5, 1, 2, 3: the
+# activation the tower's configuration names for its MLP.  Tabulated from the
+# definition to 16 digits; exact GELU(1) would be 0.8413447460685429 and the
+# identity 1.0, so a swapped activation misses these by >= 4e-3.
+QUICK_GELU_TABLE = ((-2.0, -0.06434137685579186), (-1.0, -0.1542042340671787),
+                    (-0.5, -0.1496115633936199), (0.0, 0.0), (0.5, 0.35038843660638014),
+                    (1.0, 0.8457957659328212), (2.0, 1.9356586231442083), (3.0, 2.981928690292214))
+
+
+def test_block_mlp_activation_and_fc1_bias_closed_form():
+    """Neurarch card, Structure table, ViT Block rows (MLP 5120) with the MLP
+    activation the configuration names (QuickGELU).  With W_qkv, b_qkv, W_o and
+    b_o zero the attention half adds nothing; with W_1 = 0 the MLP input is
+    u = b_1 exactly, whatever LN2 gives.  W_2 routes unit j to output column
+    j for j < 8 and b_2 is a known vector, so block(z) - z = QuickGELU(b_1[j])
+    + b_2 on those columns and b_2 elsewhere.  A different activation (exact
+    GELU, none) or a dropped fc1 bias misses the tabulated values; torch's
+    sigmoid gives the same table independently."""
+    rng = np.random.default_rng(21)
+    d, m = 1280, 5120
+    p = _block_params(rng)
+    for key in ("qkv_w", "qkv_b", "proj_w", "proj_b", "fc1_w"):
+        p[key][:] = 0
+    u = np.array([x for x, _ in QUICK_GELU_TABLE])
+    want_act = np.array([y for _, y in QUICK_GELU_TABLE])
+    p["fc1_b"] = rng.standard_normal(m)
+    p["fc1_b"][:8] = u
+    p["fc2_w"] = np.zeros((d, m))
+    p["fc2_w"][np.arange(8), np.arange(8)] = 1.0
+    p["fc2_b"] = 0.1 * rng.standard_normal(d)
+    ut = torch.tensor(u, dtype=torch.float64)
+    np.testing.assert_allclose((ut * torch.sigmoid(1.702 * ut)).numpy(), want_act, rtol=1e-14, atol=1e-16)
+    grids = [(1, 2, 4), (1, 2, 2)]
+    cu, pos, _ = O.seq_meta(grids)
+    z = rng.standard_normal((cu[-1], d))
+    want = np.tile(p["fc2_b"], (cu[-1], 1))
+    want[:, :8] += want_act
+    for rows, got in _both_block_forms(z, p, cu, O.rope_angles(pos)):
+        np.testing.assert_allclose(got - z[rows], want[rows], rtol=1e-12, atol=1e-13)
+
+
+def test_block_ln2_uses_its_own_affine_and_eps():
+    """Pre-norm MLP half: a = LN2(z) with LN2's own gain and bias and eps 1e-6
+    (Neurarch card, Structure table, ViT Block rows; LayerNorm eps of the
+    configuration).  Attention adds nothing (W_qkv, b_qkv, W_o, b_o zero).
+    Row i of z is c_i + a_i * s with s = (+1, -1, +1, ...), so its mean is c_i
+    and its biased variance a_i^2: LN2 gives s_j * r_i * g2[j] + b2ln[j] with
+    r_i = a_i / sqrt(a_i^2 + 1e-6) in closed form.  W_1 = I on the first 8
+    columns (b_1 = 0) and W_2 routes them out, so block(z) - z =
+    QuickGELU(LN2(z)[:, :8]) (activation as pinned above).  a_i down to 1e-3
+    makes eps visible (r = 0.7071 at a = 1e-3); LN1's affine is set far from
+    LN2's so borrowing it fails."""
+    rng = np.random.default_rng(22)
+    d, m = 1280, 5120
+    p = _block_params(rng)
+    for key in ("qkv_w", "qkv_b", "proj_w", "proj_b", "fc1_w", "fc1_b", "fc2_b"):
+        p[key][:] = 0
+    p["ln1_w"][:] = 3.0
+    p["ln1_b"][:] = -1.0
+    p["ln2_w"] = 1 + 0.5 * rng.standard_normal(d)
+    p["ln2_b"] = 0.5 * rng.standard_normal(d)
+    p["fc1_w"][np.arange(8), np.arange(8)] = 1.0
+    p["fc2_w"] = np.zeros((d, m))
+    p["fc2_w"][np.arange(8), np.arange(8)] = 1.0
+    grids = [(1, 2, 4)]
+    cu, pos, _ = O.seq_meta(grids)
+    s = np.where(np.arange(d) % 2 == 0, 1.0, -1.0)
+    c = np.array([0.0, 5.0, -3.0, 1e3, 0.25, -0.5, 2.0, 7.0])
+    a = np.array([1.0, 2.0, 1e-3, 0.5, 3e-3, 10.0, 1.0, 0.1])
+    z = c[:, None] + a[:, None] * s[None, :]
+    r = a / np.sqrt(a * a + 1e-6)
+    u = s[None, :8] * r[:, None] * p["ln2_w"][None, :8] + p["ln2_b"][None, :8]
+    ut = torch.from_numpy(u)
+    want = np.zeros_like(z)
+    want[:, :8] = (ut * torch.sigmoid(1.702 * ut)).numpy()
+    for rows, got in _both_block_forms(z, p, cu, O.rope_angles(pos)):
+        np.testing.assert_allclose(got - z[rows], want[rows], rtol=1e-9, atol=1e-9)
+
+
+def test_block_rope_on_q_and_k_closed_form_scores():
+    """Inside the block both q and k carry their patch's 2-D rotation and v
+    does not (Neurarch card, Structure table row "2D RoPE"; LiteRT-LM card,
+    Conversion notes: each patch carries its own 2-D rope).
+
+    q = alpha (e_0 + e_20) and k = alpha (e_0 + e_40 + e_20 + e_60) for every
+    token (from the biases, W_q = W_k = 0) touch only rotation pair 0 (angle
+    h, elements 0 and 40) and pair 20 (angle w, elements 20 and 60); rotating
+    the pair (x, y) by a gives (x cos a - y sin a, y cos a + x sin a), so
+    q_i . k_r = alpha^2 (cos D + sin D) summed over D = h_i - h_r and
+    w_i - w_r: a closed form with no rope routine in it, and not symmetric in
+    q and k (swapping them flips the sine terms).  Token l of an image is
+    z = e_{2l} - e_{2l+1}, which LN1 (gain 1, bias 0) maps to
+    kappa (e_{2l} - e_{2l+1}), kappa = 1 / sqrt(2/1280 + 1e-6); W_v row r =
+    e_{2r} then makes v_l = kappa e_l inside head 0.  W_o = I, MLP output 0,
+    so block(z) - z in head 0 column r is kappa P[i, r], the softmax over the
+    image's keys of the closed-form scores / sqrt(80).  No rotation on k (or
+    on q) makes P uniform, a rotated v leaks into columns 40..47, a wrong
+    scale or segment changes P."""
+    rng = np.random.default_rng(23)
+    d, hd, alpha = 1280, 80, 3.0
+    p = _block_params(rng)
+    for key in ("qkv_w", "qkv_b", "proj_b", "fc2_w", "fc2_b"):
+        p[key][:] = 0
+    p["ln1_w"][:] = 1.0
+    p["ln1_b"][:] = 0.0
+    p["proj_w"] = np.eye(d)
+    # q = alpha (e_0 + e_20); k = alpha (e_0 + e_40 + e_20 + e_60): head 0, pairs 0 and 20
+    p["qkv_b"][[0, 20]] = alpha
+    p["qkv_b"][d + np.array([0, 40, 20, 60])] = alpha
+    p["qkv_w"][2 * d + np.arange(8), 2 * np.arange(8)] = 1.0
+    # merge-group slot order of a 2 x 4 grid and of a 2 x 2 grid, listed by hand
+    hw = {(1, 2, 4): [(0, 0), (0, 1), (1, 0), (1, 1), (0, 2), (0, 3), (1, 2), (1, 3)],
+          (1, 2, 2): [(0, 0), (0, 1), (1, 0), (1, 1)]}
+    grids = [(1, 2, 4), (1, 2, 2)]
+    pos = np.array(hw[grids[0]] + hw[grids[1]], dtype=np.float64)
+    cu = np.array([0, 8, 12])
+    angles = rng.uniform(-3, 3, (12, hd // 2))   # pairs other than 0 and 20 play no part
+    angles[:, 0] = pos[:, 0]
+    angles[:, 20] = pos[:, 1]
+    n = 12
+    z = np.zeros((n, d))
+    local = np.concatenate([np.arange(8), np.arange(4)])
+    z[np.arange(n), 2 * local] = 1.0
+    z[np.arange(n), 2 * local + 1] = -1.0
+    kappa = 1.0 / math.sqrt(2.0 / d + 1e-6)
+    want = np.zeros((n, d))
+    for i in range(len(cu) - 1):
+        seg = np.arange(cu[i], cu[i + 1])
+        for qi in seg:
+            dh, dw = pos[qi, 0] - pos[seg, 0], pos[qi, 1] - pos[seg, 1]
+            s = alpha ** 2 * (np.cos(dh) + np.sin(dh) + np.cos(dw) + np.sin(dw)) / math.sqrt(hd)
+            e = np.exp(s - s.max())
+            want[qi, :len(seg)] = kappa * e / e.sum()
+    assert want[:8, :8].std() > 0.01            # the scores really vary across keys
+    for rows, got in _both_block_forms(z, p, cu, angles):
+        np.testing.assert_allclose(got - z[rows], want[rows], rtol=1e-10, atol=1e-12)
+
+
 # ---------------------------------------------------------------- merger
 def test_merger_identity_special_case_and_shapes():
     """fc1 = I, b1 = 0, fc2 = I[:out], b2 = 0 leaves GELU(LN(z) grouped) — pins
@@ -680,7 +829,8 @@ def test_normalize_closed_forms():
 def test_quantize_i8_hand_example():
     w = np.array([[0.5, -1.0, 0.25, 0.0],       # amax 1.0 -> scale 1/127
                   [3.0, 1.5, -0.75, 2.25],       # amax 3.0 -> scale 3/127
-                  [0.0, 0.0, 0.0, 0.0]],         # all zero -> scale 1, codes 0
+                  [0.0, 0.0, 0.0, 0.0],          # all zero -> scale 1, codes 0
+                  [127.0, 62.5, -0.5, 1.5]],     # scale exactly 1: ties 62.5 -> 62, -0.5 -> 0, 1.5 -> 2
                  dtype=np.float32)
     q, s = O.quantize_i8(w)
     assert s.dtype == np.float32 and q.dtype == np.int8
@@ -690,6 +840,7 @@ def test_quantize_i8_hand_example():
     assert q[0].tolist() == [64, -127, 32, 0]
     assert q[1].tolist() == [127, 64, -32, 95]   # 1.5/3*127 = 63.5 -> 64; 2.25/3*127 = 95.25 -> 95
     assert (q[2] == 0).all()
+    assert s[3] == 1 and q[3].tolist() == [127, 62, 0, 2]
 
 
 def test_quantize_i8_error_bound_and_extremes():
