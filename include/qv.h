@@ -33,8 +33,8 @@
  *     or frees device memory in these calls and keeps no pointer after return.
  *   - Matrices are row-major.  Linear weights use the [out][in] layout;
  *     vectors (biases, LayerNorm gain/shift) are float32 in both dtypes.
- *   - Device faults (for example a cu_seqlens array inconsistent with the grid
- *     list) surface at the caller's next synchronisation, as in any HIP library.
+ *   - Device faults surface at the caller's next synchronisation, as in any
+ *     HIP library.
  *   - Calls that overlap on the same workspace race; use one workspace per
  *     stream.
  */
@@ -60,13 +60,17 @@ typedef enum qv_status {
   QV_ERR_HIP = 6          /* a HIP runtime call or launch failed                */
 } qv_status;
 
-typedef enum qv_dtype {
+/* Element types.  qv_dtype is a plain 32-bit integer so that any value a
+ * caller passes is well defined on the library side and an unknown one is
+ * rejected with QV_ERR_UNSUPPORTED. */
+typedef int32_t qv_dtype;
+enum {
   QV_F32 = 0,  /* float32 operands and activations (correctness mode)         */
   QV_BF16 = 1, /* bf16 GEMM/attention operands, float32 accumulation,
                   residual stream, LayerNorm statistics and softmax            */
   QV_I8 = 2    /* weight format only: int8 codes [rows][cols] with one float32
                   scale per row (qv_quantize_i8)                               */
-} qv_dtype;
+};
 
 /* Text of the last non-OK status returned on the calling thread ("" if none). */
 const char *qv_last_error(void);
@@ -273,8 +277,10 @@ qv_status qv_vision_workspace_size(const qv_vision_cfg *c, const int32_t *grid_t
  *   hidden += QuickGELU(a . fc1_w^T + fc1_b) . fc2_w^T + fc2_b.
  * patches: device [N][ld] in cfg dtype, merge-group order (qv_patchify).
  * grid_thw: host [n_img][3].  cu_seqlens: device int32 [n_img + 1], the
- * prefix sums of T*gh*gw (trusted; set QV_DEBUG_VALIDATE=1 in the
- * environment to have it copied back and checked, which synchronises).
+ * prefix sums of T*gh*gw.  The kernels take every image's rows from
+ * grid_thw, so a cu_seqlens that disagrees with it cannot move an access
+ * out of bounds; set QV_DEBUG_VALIDATE=1 in the environment to have it
+ * copied back and compared (QV_ERR_SHAPE on a mismatch; this synchronises).
  * hidden: device out float32 [N][dim] (the residual stream after the last
  * block, before the merger).  ws: device workspace of ws_bytes.
  * Errors: QV_ERR_NULL, QV_ERR_SHAPE, QV_ERR_UNSUPPORTED, QV_ERR_WORKSPACE,

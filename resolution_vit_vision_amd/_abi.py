@@ -12,7 +12,9 @@ import re
 from ctypes import POINTER, Structure, c_char_p, c_float, c_int32, c_int64, c_size_t, c_uint64, c_void_p
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libqv.so")
+# QV_LIBRARY names another build of the same ABI (the host-only sanitizer build
+# of the test suite); by default the library next to this file.
+LIB_PATH = os.environ.get("QV_LIBRARY") or os.path.join(HERE, "libqv.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "qv.h")
 
 QV_OK, QV_ERR_NULL, QV_ERR_SHAPE, QV_ERR_BUDGET, QV_ERR_WORKSPACE, QV_ERR_UNSUPPORTED, QV_ERR_HIP = range(7)

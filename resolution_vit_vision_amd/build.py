@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqv.so")
-SOURCES = ["host.cpp", "misc.hip", "gemm.hip", "attention.hip"]
+SOURCES = ["host.cpp", "plan.cpp", "misc.hip", "gemm.hip", "attention.hip"]
 # The attention kernel rescales and reads its MFMA accumulators every key
 # block; keeping them in arch VGPRs avoids AGPR<->VGPR copies on each use.
 EXTRA_FLAGS = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}

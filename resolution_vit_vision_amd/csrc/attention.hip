@@ -115,8 +115,8 @@ __global__ __launch_bounds__(512) void k_attn_bf16(AttnArgs a, float scale_log2)
     }
   }
   const PlanEntry pe = a.plan[find_plan(a.plan, a.n_img, gt)];
-  const int row0 = a.out_row ? 0 : a.cu_seqlens[pe.seg];
-  const int n = a.out_row ? pe.n : a.cu_seqlens[pe.seg + 1] - row0;
+  const int row0 = a.out_row ? 0 : pe.row0;
+  const int n = pe.n;
   const int qbase = (gt - pe.qtile0) * BQ + qw * 32;
 
   const uint16_t* Qh = reinterpret_cast<const uint16_t*>(a.q) + (size_t)head * a.P * kHeadDim;
@@ -394,8 +394,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
     }
   }
   const PlanEntry pe = a.plan[find_plan(a.plan, a.n_img, gt)];
-  const int row0 = a.out_row ? 0 : a.cu_seqlens[pe.seg];
-  const int n = a.out_row ? pe.n : a.cu_seqlens[pe.seg + 1] - row0;
+  const int row0 = a.out_row ? 0 : pe.row0;
+  const int n = pe.n;
   const int qbase = (gt - pe.qtile0) * BQ + wave * 32;
 
   const uint16_t* Qh = reinterpret_cast<const uint16_t*>(a.q) + (size_t)head * a.P * kHeadDim;
@@ -635,11 +635,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
 
 #pragma clang diagnostic pop
 
-int attention_bf16_rows_per_wg(int64_t wgs_at_128) {
-  // 128 query rows per workgroup when that alone gives a workgroup per CU,
-  // else 64 (the key split doubles the workgroups)
-  return wgs_at_128 >= 256 ? 128 : 64;
-}
 
 hipError_t attention_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.total_qtiles == 0) return hipSuccess;
@@ -807,8 +802,8 @@ __global__ __launch_bounds__(64) void k_attn_f32(AttnArgs a, float scale) {
   const int lane = threadIdx.x;
   const int head = blockIdx.y, gt = blockIdx.x;
   const PlanEntry pe = a.plan[find_plan(a.plan, a.n_img, gt)];
-  const int row0 = a.out_row ? 0 : a.cu_seqlens[pe.seg];
-  const int n = a.out_row ? pe.n : a.cu_seqlens[pe.seg + 1] - row0;
+  const int row0 = a.out_row ? 0 : pe.row0;
+  const int n = pe.n;
   const int q = (gt - pe.qtile0) * FBQ + lane;
   const float* Qh = reinterpret_cast<const float*>(a.q) + (size_t)head * a.P * kHeadDim;
   const float* Kh = reinterpret_cast<const float*>(a.k) + (size_t)head * a.P * kHeadDim;

@@ -716,18 +716,6 @@ hipError_t gemm_bf16_resid_f32(const void* A, int lda, const void* B, int ldb, i
   return run_bf16(A, lda, B, ldb, M, N, K, EpiResidF32{Z, ldz, bias}, RowMapIdentity{}, s);
 }
 
-// Split-K for narrow outputs at small M: 128x160 tiles (warp-specialized)
-// with the K range cut into `splits` runs, one workgroup per (tile, run),
-// so the grid fills the 256 CUs where the plain tiling has 64 tiles.
-int gemm_splitk_runs(int M, int N, int K) {
-  if (N % 160 || K % 64) return 1;
-  const int64_t tiles = (int64_t)((M + 127) / 128) * (N / 160);
-  for (int s : {4, 2}) {
-    const int kt = K / 64 / s;
-    if ((K / 64) % s == 0 && tiles * s <= 256 && (kt == 20 || kt == 40)) return s;
-  }
-  return 1;
-}
 
 hipError_t gemm_bf16_splitk_f32(const void* A, int lda, const void* B, int ldb, int M, int N, int K, int splits,
                                 float* P, hipStream_t s) {
@@ -739,24 +727,6 @@ hipError_t gemm_bf16_splitk_f32(const void* A, int lda, const void* B, int ldb, 
     case 40: return launch_ws<128, 160, 4, 1, 4, 40, 4>(A, lda, B, ldb, M, N, e, RowMapIdentity{}, s, splits);
     default: return hipErrorInvalidValue;
   }
-}
-// Split-K for a product whose output alone leaves most CUs idle (the
-// merger's two Linears at small M): 128 x 160 tiles when N allows, else
-// 128 x 128; the float32 partial sums are reduced by launch_splitk_reduce.
-int gemm_splitk_any_runs(int M, int N, int K) {
-  if (K % 64) return 1;
-  const int kt = K / 64;
-  const int64_t mt = (M + 127) / 128;
-  if (N % 160 == 0) {
-    for (int s : {4, 2})
-      if (kt % s == 0 && mt * (N / 160) * s <= 256 && (kt / s == 20 || kt / s == 40)) return s;
-    return 1;
-  }
-  if (N % 128 == 0) {
-    for (int s : {8, 4, 2})
-      if (kt % s == 0 && mt * (N / 128) * s <= 256 && (kt / s == 10 || kt / s == 20 || kt / s == 40)) return s;
-  }
-  return 1;
 }
 
 hipError_t gemm_bf16_splitk_any_f32(const void* A, int lda, const void* B, int ldb, int M, int N, int K, int splits,
@@ -868,16 +838,6 @@ hipError_t gemm_i8w_act_bf16(const void* A, int lda, const int8_t* B, int ldb, c
                                                 RowMapIdentity{}, s);
 }
 
-// K runs for an int8-weight GEMM of N = 1280 (1 = no split): the largest of
-// 4 and 2 whose workgroups still fit one per CU.
-int gemm_i8w_runs(int M, int N, int K) {
-  if (N % 160 || K % 64) return 1;
-  const int64_t tiles = (int64_t)((M + 127) / 128) * (N / 160);
-  const int kt = K / 64;
-  for (int s : {4, 2})
-    if (tiles * s <= 256 && kt % s == 0 && (kt / s == 20 || kt / s == 10 || kt / s == 5)) return s;
-  return 1;
-}
 
 hipError_t gemm_i8w_splitk_f32(const void* A, int lda, const int8_t* B, int ldb, const float* scale, int M, int N,
                                int K, int splits, float* P, hipStream_t s) {
@@ -941,9 +901,6 @@ struct EpiColScale {
   }
 };
 
-bool gemm_i8w_wide(int M, int N) {
-  return (int64_t)((M + 255) / 256) * ((N + 255) / 256) >= 160;  // the bf16 rule in run_pipe
-}
 
 template <int KT, class Epi, class RowMap>
 static hipError_t launch_i8_wide(const void* A, int lda, const void* codes, int ldb, const float* scale, int M, int N,

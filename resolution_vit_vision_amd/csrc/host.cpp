@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <mutex>
 #include <string>
@@ -46,7 +47,7 @@ thread_local LaunchTiming* g_launch_timing = nullptr;
 namespace {
 struct Timing {
   std::mutex mu;
-  int cls = -1;
+  std::atomic<int> cls{-1};  // read without the lock on every launch; written under it
   std::vector<std::pair<hipEvent_t, hipEvent_t>> pool;
   size_t used = 0;
 };
@@ -59,8 +60,9 @@ Timing& timing() {
 // nullptr when that class is not being timed.
 std::pair<hipEvent_t, hipEvent_t>* timing_slot(int cls) {
   Timing& t = timing();
-  if (t.cls != cls) return nullptr;
+  if (t.cls.load(std::memory_order_relaxed) != cls) return nullptr;
   std::lock_guard<std::mutex> g(t.mu);
+  if (t.cls.load(std::memory_order_relaxed) != cls) return nullptr;
   if (t.used == t.pool.size()) {
     hipEvent_t a, b;
     if (hipEventCreate(&a) != hipSuccess) return nullptr;
@@ -406,7 +408,7 @@ qv_status make_plan(const qv_vision_cfg* c, const int32_t* grid_thw, int32_t n_i
   int qt = 0;
   for (int k = 0; k < n_img; ++k) {
     const ImgDesc& d = vp.desc[order[k]];
-    vp.plan[k] = PlanEntry{order[k], d.prow0, qt, 0};
+    vp.plan[k] = PlanEntry{d.row0, d.prow0, qt, d.n};
     qt += (int)((d.n + bq - 1) / bq);
   }
   vp.total_qtiles = qt;
@@ -601,9 +603,9 @@ qv_status qv_vision_forward(const qv_vision_cfg* c, const qv_vision_w* w, const 
     QV_LAUNCH(QV_KC_PATCH_EMBED, s, gemm_f32_store(reinterpret_cast<const float*>(patches), c->ld, reinterpret_cast<const float*>(w->patch_w),
                           c->patch_dim, M, D, c->patch_dim, reinterpret_cast<const float*>(w->patch_b), hidden, D, s));
 
-  AttnArgs aa{qo.q, qo.k, qo.vt, O, D, cu_seqlens, plan, n_img, nullptr, (int)vp.P, c->heads, vp.total_qtiles,
+  AttnArgs aa{qo.q, qo.k, qo.vt, O, D, plan, n_img, nullptr, (int)vp.P, c->heads, vp.total_qtiles,
               vp.attn_rows};
-  AttnArgs aw{qo.q, qo.k, qo.vt, O, D, cu_seqlens, planw, (int)vp.n_win, outrow, (int)vp.Pw, c->heads,
+  AttnArgs aw{qo.q, qo.k, qo.vt, O, D, planw, (int)vp.n_win, outrow, (int)vp.Pw, c->heads,
               vp.total_qtiles_w, bf ? 64 : kAttnBQ_f32};
   // Split-K (small M): fc2 leaves float32 partial sums; the next block's
   // first LayerNorm adds them, the bias and the residual in a fixed order

@@ -56,14 +56,14 @@ struct DescChunk {
 };
 
 // One entry of the attention work plan, segments sorted by length, longest
-// first.  A segment is an image (rows cu_seqlens[seg] .. cu_seqlens[seg+1])
-// or, for windowed blocks, one window (length in `n`, output rows through
-// the out_row map).
+// first.  A segment is an image (packed rows row0 .. row0 + n, taken from
+// the host's grid list, never from the caller's device cu_seqlens) or, for
+// windowed blocks, one window (output rows through the out_row map).
 struct PlanEntry {
-  int32_t seg;        // image index (into cu_seqlens) or window index
+  int32_t row0;       // image plans: first packed row; window plans: window index
   int32_t prow0;      // padded row start
   int32_t qtile0;     // first global q-tile of this segment
-  int32_t n;          // window length (window plans only)
+  int32_t n;          // rows of the segment (patches of the image, or of the window)
 };
 
 // Patchify: one image per chunk entry.
@@ -193,7 +193,6 @@ struct AttnArgs {
   const void* vt;
   void* o;
   int ldo;
-  const int32_t* cu_seqlens;
   const PlanEntry* plan;
   int n_img;                 // plan entries (images or windows)
   const int32_t* out_row;    // null: segments are images; else window plan, packed row of each padded row

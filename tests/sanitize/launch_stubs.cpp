@@ -1,0 +1,50 @@
+// Launcher stubs for the host-only sanitizer build of the C ABI.
+//
+// Every kernel launcher of the library is replaced by a function that checks
+// nothing (apart from reading the host memory the real one reads) and returns
+// hipSuccess, so host.cpp's validation, planning and
+// workspace carving run to completion under AddressSanitizer and
+// UndefinedBehaviorSanitizer on a machine without a GPU.  Device pointers
+// handed to these stubs are never dereferenced.
+#include "qv_internal.h"
+
+namespace qv {
+hipError_t launch_fold_weight(const void* w, int dim, int channels, int patch, int temporal, int ld_in, void* out, int ld_out, bool bf16, hipStream_t s) { return hipSuccess; }
+hipError_t launch_patchify(const float* pixels, const PatchChunk& c, int patch, int temporal, void* out, bool bf16, int ld, const PatchMode& m, int64_t rows_in_chunk_max, hipStream_t s) { return hipSuccess; }
+hipError_t launch_setup_tokens(const DescChunk& c, int2* tokinfo, hipStream_t s) { return hipSuccess; }
+hipError_t launch_setup_windows(const DescChunk& c, int window, int slot, int2* tokinfo_w, int32_t* out_row, hipStream_t s) { return hipSuccess; }
+hipError_t launch_setup_plan(const PlanEntry* host_plan_chunk, int count, int first, PlanEntry* plan, hipStream_t s) {
+  // the real launcher copies `count` host entries into kernel arguments: read them
+  volatile int32_t sink = 0;
+  for (int i = 0; i < count; ++i) sink = sink + host_plan_chunk[i].row0 + host_plan_chunk[i].n;
+  (void)sink;
+  return hipSuccess;
+}
+hipError_t launch_rope_table(float2* tab, int positions, float theta, hipStream_t s) { return hipSuccess; }
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) { return hipSuccess; }
+hipError_t launch_layernorm(const float* x, const float* g, const float* b, void* y, bool bf16, int rows, int dim, float eps, hipStream_t s) { return hipSuccess; }
+hipError_t gemm_bf16_store_f32(const void* A, int lda, const void* B, int ldb, int M, int N, int K, const float* bias, float* C, int ldc, hipStream_t s) { return hipSuccess; }
+hipError_t gemm_bf16_resid_f32(const void* A, int lda, const void* B, int ldb, int M, int N, int K, const float* bias, float* Z, int ldz, hipStream_t s) { return hipSuccess; }
+hipError_t gemm_i8w_qkv(const void* A, int lda, const int8_t* B, int ldb, const float* scale, int M, int K, const float* bias, const QkvOut& o, hipStream_t s) { return hipSuccess; }
+hipError_t gemm_i8w_act_bf16(const void* A, int lda, const int8_t* B, int ldb, const float* scale, int M, int N, int K, const float* bias, Act act, void* C, int ldc, hipStream_t s) { return hipSuccess; }
+hipError_t gemm_i8w_splitk_f32(const void* A, int lda, const int8_t* B, int ldb, const float* scale, int M, int N, int K, int splits, float* P, hipStream_t s) { return hipSuccess; }
+hipError_t gemm_i8w_resid_f32(const void* A, int lda, const int8_t* B, int ldb, const float* scale, int M, int N, int K, const float* bias, float* Z, int ldz, hipStream_t s) { return hipSuccess; }
+hipError_t launch_quantize_i8(const void* w, int rows, int cols, int ld, bool bf16, int8_t* q, float* scale, hipStream_t s) { return hipSuccess; }
+hipError_t launch_codes_bf16(const int8_t* q, int64_t n, void* out, hipStream_t s) { return hipSuccess; }
+hipError_t gemm_i8w_wide_qkv(const void* A, int lda, const void* codes, int ldb, const float* scale, int M, int K, const float* bias, const QkvOut& o, hipStream_t s) { return hipSuccess; }
+hipError_t gemm_i8w_wide_act_bf16(const void* A, int lda, const void* codes, int ldb, const float* scale, int M, int N, int K, const float* bias, Act act, void* C, int ldc, hipStream_t s) { return hipSuccess; }
+hipError_t gemm_i8w_wide_resid_f32(const void* A, int lda, const void* codes, int ldb, const float* scale, int M, int N, int K, const float* bias, float* Z, int ldz, hipStream_t s) { return hipSuccess; }
+hipError_t gemm_bf16_splitk_any_f32(const void* A, int lda, const void* B, int ldb, int M, int N, int K, int splits, float* P, hipStream_t s) { return hipSuccess; }
+hipError_t launch_splitk_reduce(const float* P, int splits, size_t stride, const float* bias, Act act, void* out, int ldo, int M, int N, hipStream_t s) { return hipSuccess; }
+hipError_t gemm_bf16_splitk_f32(const void* A, int lda, const void* B, int ldb, int M, int N, int K, int splits, float* P, hipStream_t s) { return hipSuccess; }
+hipError_t launch_layernorm_acc(float* x, const float* parts, size_t part_stride, int splits, const float* pb, const float* g, const float* b, void* y, bool bf16, int rows, int dim, float eps, hipStream_t s) { return hipSuccess; }
+hipError_t gemm_bf16_act_bf16(const void* A, int lda, const void* B, int ldb, int M, int N, int K, const float* bias, Act act, void* C, int ldc, hipStream_t s) { return hipSuccess; }
+hipError_t gemm_bf16_qkv(const void* A, int lda, const void* B, int ldb, int M, int K, const float* bias, const QkvOut& o, hipStream_t s) { return hipSuccess; }
+hipError_t gemm_f32_store(const float* A, int lda, const float* B, int ldb, int M, int N, int K, const float* bias, float* C, int ldc, hipStream_t s) { return hipSuccess; }
+hipError_t gemm_f32_resid(const float* A, int lda, const float* B, int ldb, int M, int N, int K, const float* bias, float* Z, int ldz, hipStream_t s) { return hipSuccess; }
+hipError_t gemm_f32_act(const float* A, int lda, const float* B, int ldb, int M, int N, int K, const float* bias, Act act, float* C, int ldc, hipStream_t s) { return hipSuccess; }
+hipError_t rope_scatter_f32(const float* qkv, int M, const float* bias_unused, const QkvOut& o, hipStream_t s) { return hipSuccess; }
+hipError_t attention_bf16(const AttnArgs& a, hipStream_t s) { return hipSuccess; }
+hipError_t attention_bf16_windows(const AttnArgs& a, hipStream_t s) { return hipSuccess; }
+hipError_t attention_f32(const AttnArgs& a, hipStream_t s) { return hipSuccess; }
+}  // namespace qv
