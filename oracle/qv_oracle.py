@@ -295,10 +295,12 @@ def rope_angles(pos: np.ndarray, head_dim: int = 80, theta: float = 1e4) -> np.n
 def apply_rope(x: np.ndarray, angles: np.ndarray) -> np.ndarray:
     """Rotate each head vector: x'[j] = x[j] cos a_j - x[j+half] sin a_j,
     x'[j+half] = x[j+half] cos a_j + x[j] sin a_j.  x is [N][heads][hd],
-    angles [N][hd/2]; cos/sin are taken in float64."""
+    angles [N][hd/2]; cos/sin are evaluated in float64 and used in the
+    working precision of x (float64 by default; float32 tables in the float32
+    mode, as the rotary tables of the float32 path are)."""
     half = x.shape[-1] // 2
-    c = np.cos(angles)[:, None, :]
-    s = np.sin(angles)[:, None, :]
+    c = np.cos(angles).astype(x.dtype, copy=False)[:, None, :]
+    s = np.sin(angles).astype(x.dtype, copy=False)[:, None, :]
     x1 = x[..., :half]
     x2 = x[..., half:]
     return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)

@@ -65,3 +65,13 @@ def test_traffic_only_for_the_recorded_sources(monkeypatch):
     assert bench.traffic_for("fc2", "qwen2vl_2b_448") is None
     if rec is not None:  # recorded for the sources in the tree: a plausible byte count
         assert 10e6 < rec < 1e9
+
+
+def test_extrapolated_cpu_baseline_fields():
+    """The sampled oracle baseline runs on the CPU and reports itself as
+    extrapolated, with a positive rate and the sample it was scaled from."""
+    wl = synth.small_workload("ex", [(224, 224, 1)], depth=2)
+    params, imgs = synth.params(wl), synth.pixels(wl)
+    r = bench.cpu_baseline_extrapolated(wl, params, imgs, rows=(32, 128), merge_groups=16)
+    assert r["kind"] == "oracle" and r["extrapolated"] is True and r["unit"] == "tokens/s"
+    assert r["value"] > 0 and r["seconds_estimated_forward"] > 0 and "extrapolated" in r["sample"]

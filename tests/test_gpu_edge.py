@@ -85,3 +85,34 @@ def test_odd_frame_count_video_repeats_last_frame():
     """5 frames: T = 3 temporal patches, the last one pairing frame 4 with
     itself."""
     _check([(56, 84, 5)], 2, "bf16")
+
+
+def test_inconsistent_cu_seqlens_is_harmless_and_flagged():
+    """The kernels take each image's rows from the host grid list: a device
+    cu_seqlens that disagrees with it (every entry inside the buffer, only
+    the boundaries wrong) leaves the output bit for bit unchanged, and the
+    debug validation reports it as QV_ERR_SHAPE."""
+    import os
+    qv = _qv()
+    from resolution_vit_vision_amd import _abi
+    images = [(84, 140, 1), (56, 56, 1), (112, 84, 1)]
+    wl = synth.small_workload("cu", images, depth=1)
+    enc = qv.Encoder(synth.params(wl), synth.pixels(wl), depth=1, out_dim=1536)
+    enc.run()
+    torch.cuda.synchronize()
+    h1 = enc.hidden.clone()
+    good = enc.cu.clone()
+    wrong = torch.tensor([0, 4, 8, int(good[-1])], dtype=good.dtype, device=good.device)
+    enc.cu.copy_(wrong)
+    enc.run()
+    torch.cuda.synchronize()
+    assert torch.equal(h1, enc.hidden)
+    os.environ["QV_DEBUG_VALIDATE"] = "1"
+    try:
+        with pytest.raises(_abi.QvError) as ei:
+            enc.run()
+        assert ei.value.status == _abi.QV_ERR_SHAPE
+    finally:
+        del os.environ["QV_DEBUG_VALIDATE"]
+        enc.cu.copy_(good)
+        torch.cuda.synchronize()

@@ -2,10 +2,12 @@
 
 Integers and the patch matrix are compared bit for bit; floating-point
 outputs by relative L2 error over the whole tensor, accumulated in float64:
-<= 2e-2 for the bf16 path and <= 1e-4 for the float32 path.  Small cases run
-the oracle end to end; the full-size workloads check patchify exactly, then
-one block at the start and one at the end teacher-forced (the oracle block
-fed the GPU's own input) on sampled rows, and the merger on sampled groups."""
+<= 2e-2 for the bf16 path and <= 1e-4 for the float32 path.  Small cases,
+the 448x448 image and the four packed 672x672 images run the oracle end to
+end over whole tensors; the larger workloads check patchify exactly, then
+nine blocks spread over the depth teacher-forced (the oracle block fed the
+GPU's own input) on rows covering every 128-row query tile, and the merger
+on the groups of those rows."""
 import sys
 
 import numpy as np
@@ -200,26 +202,74 @@ def test_full_448_end_to_end(fold):
     assert e_z <= wl.tol and e_o <= wl.tol
 
 
-def _sampled_rows(cu, rng, per_image=4):
+def test_full_672x4_end_to_end():
+    """Four 672x672 images packed varlen (cu_seqlens 0, 2304, ..., 9216)
+    through all 32 blocks and the merger in the benchmark's launch
+    configuration (Conv2d fold), compared with the oracle's whole encoder
+    (float64, Conv3d definition) over the whole hidden and merged tensors,
+    and image by image."""
+    qv = _qv()
+    wl = synth.W672X4
+    _say(f"{wl.name}: drawing params")
+    params = synth.params(wl)
+    imgs = synth.pixels(wl)
+    enc = qv.Encoder(params, imgs, depth=wl.depth, out_dim=wl.out_dim, dtype=wl.dtype, fold=True)
+    enc.run()
+    torch.cuda.synchronize()
+    grids = [O.grid_thw(h, w, f)[2] for h, w, f in wl.images]
+    assert enc.grids == [(1, 48, 48)] * 4
+    _say(f"{wl.name}: oracle (float64, 32 blocks, 9216 patches)")
+    z, out = _oracle_encode(imgs, params, grids, wl.depth)
+    hid, mo = _host(enc.hidden), _host(enc.out)
+    e_z, e_o = rel_l2(hid, z), rel_l2(mo, out)
+    _say(f"  hidden rel-L2 {e_z:.3e}  merged rel-L2 {e_o:.3e}")
+    assert out.shape == (2304, 1536) and mo.shape == (2304, 1536)
+    assert e_z <= wl.tol and e_o <= wl.tol
+    for i in range(4):
+        a, b = 2304 * i, 2304 * (i + 1)
+        ei = rel_l2(hid[a:b], z[a:b])
+        _say(f"  image {i}: hidden rel-L2 {ei:.3e}")
+        assert ei <= wl.tol and rel_l2(mo[a // 4:b // 4], out[a // 4:b // 4]) <= wl.tol
+
+
+def _band_rows(cu, rng, band=128, per_image=64):
+    """Rows to check: in every image, one random row from each band of 128
+    rows (the attention kernels' query tiles), the first and last rows, and
+    further random rows up to `per_image`."""
     rows = []
     for i in range(len(cu) - 1):
         a, b = int(cu[i]), int(cu[i + 1])
-        rows += [a, b - 1] + list(rng.integers(a, b, size=per_image))
+        mine = {a, b - 1}
+        for lo in range(a, b, band):
+            mine.add(int(rng.integers(lo, min(lo + band, b))))
+        extra = max(0, min(per_image, b - a) - len(mine))
+        rest = np.setdiff1d(np.arange(a, b), np.fromiter(mine, dtype=np.int64))
+        mine.update(int(x) for x in rng.choice(rest, size=extra, replace=False))
+        rows += sorted(mine)
     return np.unique(np.asarray(rows))
 
 
-FULL = [(n, "dtype") for n in ("qwen2vl_2b_672x4_varlen", "mixed16_varlen_7b_merger", "maxres_3584",
-                                "qwen25vl_7b_3584_window", "video_448_16f")]
+# blocks teacher-forced at full size: spread over the depth, including the
+# Qwen2.5-VL full-attention blocks 7/15/23/31 of the windowed workload
+DEEP_BLOCKS = (0, 4, 7, 11, 15, 19, 23, 27, 31)
+LIGHT_BLOCKS = (0, 7, 15, 23, 31)
+
+FULL = [(n, "dtype", DEEP_BLOCKS) for n in ("qwen2vl_2b_672x4_varlen", "mixed16_varlen_7b_merger", "maxres_3584",
+                                             "qwen25vl_7b_3584_window")]
+FULL += [("video_448_16f", "dtype", LIGHT_BLOCKS)]
 # int8 block matrices at full size (bench --weights int8): the blocks are
 # checked against the oracle on the dequantized weights
-FULL += [("qwen2vl_2b_672x4_varlen", "int8"), ("qwen25vl_7b_3584_window", "int8")]
+FULL += [("qwen2vl_2b_672x4_varlen", "int8", LIGHT_BLOCKS), ("qwen25vl_7b_3584_window", "int8", LIGHT_BLOCKS)]
 
 
-@pytest.mark.parametrize("name,weights", FULL, ids=[n if w == "dtype" else f"{n}-int8" for n, w in FULL])
-def test_full_size_sampled(name, weights):
+@pytest.mark.parametrize("name,weights,blocks", FULL, ids=[n if w == "dtype" else f"{n}-int8" for n, w, _ in FULL])
+def test_full_size_sampled(name, weights, blocks):
     """Full-size workload in the benchmark's launch configuration (still
-    images take the Conv2d fold there): exact patchify and metadata; first
-    and last block teacher-forced on sampled rows; merger on sampled groups."""
+    images take the Conv2d fold there): exact patchify and metadata; blocks
+    spread over the depth teacher-forced (the oracle block fed the GPU's own
+    input) on rows that cover every 128-row query tile of every image (at
+    least 64 rows per image; 512+ at 3584x3584); merger on the groups of
+    those rows."""
     qv = _qv()
     wl = synth.WORKLOADS[name]
     _say(f"{name} weights={weights}: drawing inputs")
@@ -244,19 +294,22 @@ def test_full_size_sampled(name, weights):
     out_full = _host(enc.out)
     hid_full = _host(enc.hidden)
     angles = O.rope_angles(pos)
-    rows = _sampled_rows(cu, rng)
-    for l in ((0, wl.depth - 1) if not wl.window else (0, wl.full_blocks[0], wl.depth - 1)):
+    rows = _band_rows(cu, rng)
+    assert len(rows) >= min(512, cu[-1])
+    errs = {}
+    for l in blocks:
         z_in = _host(qv.vision_forward(enc.vcfg.__class__(**{**enc.vcfg.__dict__, "depth": l}), enc.vw,
                                        enc.patches, enc.grids, enc.cu, ws=enc.ws)).astype(np.float64)
         z_out = _host(qv.vision_forward(enc.vcfg.__class__(**{**enc.vcfg.__dict__, "depth": l + 1}), enc.vw,
                                         enc.patches, enc.grids, enc.cu, ws=enc.ws))
         torch.cuda.synchronize()
         groups = windows if (windows is not None and l not in wl.full_blocks) else None
-        _say(f"{name}: block {l} ({'windowed' if groups else 'full'}) teacher-forced on {len(rows)} rows")
         ref = O.vision_block_rows(z_in, O.block_params(block_ref, l), cu, angles, rows, groups=groups)
         e = rel_l2(z_out[rows], ref)
-        _say(f"  block {l} rel-L2 {e:.3e}")
-        assert e <= wl.tol
+        errs[l] = e
+        _say(f"{name}: block {l} ({'windowed' if groups else 'full'}) teacher-forced on {len(rows)} rows: "
+             f"rel-L2 {e:.3e}")
+    assert max(errs.values()) <= wl.tol, errs
     groups = np.unique(rows // 4)
     zr = np.concatenate([hid_full[4 * g:4 * g + 4] for g in groups])
     ref = O.patch_merge(zr.astype(np.float64), params)
