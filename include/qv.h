@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define QV_ABI_VERSION 3
+#define QV_ABI_VERSION 4
 
 typedef enum qv_status {
   QV_OK = 0,
@@ -288,6 +288,29 @@ qv_status qv_vision_workspace_size(const qv_vision_cfg *c, const int32_t *grid_t
 qv_status qv_vision_forward(const qv_vision_cfg *c, const qv_vision_w *w, const void *patches,
                             const int32_t *grid_thw, int32_t n_img, const int32_t *cu_seqlens,
                             float *hidden, void *ws, size_t ws_bytes, void *stream);
+
+/* Size of the static device workspace behind qv_vision_forward_noalloc. */
+#define QV_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* Encoder forward that allocates nothing, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same computation, arguments, output and
+ * errors as qv_vision_forward, without ws / ws_bytes: the workspace is a
+ * static device array of QV_SCRATCH_BYTES (64 MiB) compiled into the
+ * library, one copy on every GPU the library runs on, held until the process
+ * ends.  A call whose qv_vision_workspace_size exceeds it returns
+ * QV_ERR_WORKSPACE before anything is enqueued (a 448x448 image needs
+ * 42.5 MiB, a 672x672 image 50.7 MiB; four packed 672x672 images do not
+ * fit).  The array of the device current at the call is used, so `stream`
+ * must belong to that device; its address is looked up on the first call on
+ * each device.  Every call on one GPU shares that GPU's array and leaves its
+ * own contents there; each call initialises everything it reads, so nothing
+ * carries over, but two calls whose work overlaps on one GPU (two streams,
+ * or two host threads) race on the array: serialise them.  No hipMalloc,
+ * hipFree or other allocating call is made. */
+qv_status qv_vision_forward_noalloc(const qv_vision_cfg *c, const qv_vision_w *w, const void *patches,
+                                    const int32_t *grid_thw, int32_t n_img, const int32_t *cu_seqlens,
+                                    float *hidden, void *stream);
 
 /* Symmetric per-row int8 weights (LiteRT-LM card, model table, Vision and
  * Adapter rows: int8 weights; the grouping and rounding are this library's

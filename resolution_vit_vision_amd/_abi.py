@@ -19,6 +19,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "qv.h")
 
 QV_OK, QV_ERR_NULL, QV_ERR_SHAPE, QV_ERR_BUDGET, QV_ERR_WORKSPACE, QV_ERR_UNSUPPORTED, QV_ERR_HIP = range(7)
 QV_F32, QV_BF16, QV_I8 = 0, 1, 2
+QV_SCRATCH_BYTES = 64 << 20   # static workspace of qv_vision_forward_noalloc
 STATUS_NAMES = {0: "QV_OK", 1: "QV_ERR_NULL", 2: "QV_ERR_SHAPE", 3: "QV_ERR_BUDGET", 4: "QV_ERR_WORKSPACE",
                 5: "QV_ERR_UNSUPPORTED", 6: "QV_ERR_HIP"}
 
@@ -131,6 +132,9 @@ def lib() -> ctypes.CDLL:
     L.qv_vision_forward.restype = c_int32
     L.qv_vision_forward.argtypes = [POINTER(VisionCfg), POINTER(VisionW), c_void_p, c_void_p, c_int32, c_void_p,
                                     c_void_p, c_void_p, c_size_t, c_void_p]
+    L.qv_vision_forward_noalloc.restype = c_int32
+    L.qv_vision_forward_noalloc.argtypes = [POINTER(VisionCfg), POINTER(VisionW), c_void_p, c_void_p, c_int32,
+                                            c_void_p, c_void_p, c_void_p]
     L.qv_merge_workspace_size.restype = c_int32
     L.qv_merge_workspace_size.argtypes = [POINTER(MergerCfg), c_int64, POINTER(c_size_t)]
     L.qv_patch_merge.restype = c_int32

@@ -526,10 +526,16 @@ qv_status qv_vision_workspace_size(const qv_vision_cfg* c, const int32_t* grid_t
   return QV_OK;
 }
 
-qv_status qv_vision_forward(const qv_vision_cfg* c, const qv_vision_w* w, const void* patches,
-                            const int32_t* grid_thw, int32_t n_img, const int32_t* cu_seqlens, float* hidden,
-                            void* ws, size_t ws_bytes, void* stream) {
-  if (!w || !patches || !cu_seqlens || !hidden || !ws)
+}  // extern "C"
+
+namespace {
+// Body of qv_vision_forward and qv_vision_forward_noalloc: validation, the
+// plan, then every launch on `stream`.  use_scratch: the workspace is the
+// library's static device array instead of the caller's ws.
+qv_status vision_forward_impl(const qv_vision_cfg* c, const qv_vision_w* w, const void* patches,
+                              const int32_t* grid_thw, int32_t n_img, const int32_t* cu_seqlens, float* hidden,
+                              void* ws, size_t ws_bytes, bool use_scratch, void* stream) {
+  if (!w || !patches || !cu_seqlens || !hidden || (!ws && !use_scratch))
     return fail(QV_ERR_NULL, "weights, patches, cu_seqlens, hidden and ws must be non-NULL");
   VisionPlan vp;
   qv_status st = make_plan(c, grid_thw, n_img, vp);
@@ -539,6 +545,16 @@ qv_status qv_vision_forward(const qv_vision_cfg* c, const qv_vision_w* w, const 
   for (int l = 0; l < c->depth; ++l) {
     st = check_block(w->blocks[l], l, vp.i8);
     if (st != QV_OK) return st;
+  }
+  if (use_scratch) {
+    if (vp.total > QV_SCRATCH_BYTES)
+      return fail(QV_ERR_WORKSPACE, "this batch needs %zu bytes of workspace, above the %zu-byte static scratch of "
+                  "the allocation-free forward (use qv_vision_forward with a caller workspace)",
+                  vp.total, (size_t)QV_SCRATCH_BYTES);
+    void* p = nullptr;
+    QV_HIP(scratch_buffer(&p));
+    ws = p;
+    ws_bytes = QV_SCRATCH_BYTES;
   }
   if (ws_bytes < vp.total)
     return fail(QV_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, vp.total);
@@ -716,6 +732,21 @@ qv_status qv_vision_forward(const qv_vision_cfg* c, const qv_vision_w* w, const 
     pending = 0;
   }
   return QV_OK;
+}
+}  // namespace
+
+extern "C" {
+
+qv_status qv_vision_forward(const qv_vision_cfg* c, const qv_vision_w* w, const void* patches,
+                            const int32_t* grid_thw, int32_t n_img, const int32_t* cu_seqlens, float* hidden,
+                            void* ws, size_t ws_bytes, void* stream) {
+  return vision_forward_impl(c, w, patches, grid_thw, n_img, cu_seqlens, hidden, ws, ws_bytes, false, stream);
+}
+
+qv_status qv_vision_forward_noalloc(const qv_vision_cfg* c, const qv_vision_w* w, const void* patches,
+                                    const int32_t* grid_thw, int32_t n_img, const int32_t* cu_seqlens,
+                                    float* hidden, void* stream) {
+  return vision_forward_impl(c, w, patches, grid_thw, n_img, cu_seqlens, hidden, nullptr, 0, true, stream);
 }
 
 static qv_status check_merger_cfg(const qv_merger_cfg* c, int64_t n_tokens) {

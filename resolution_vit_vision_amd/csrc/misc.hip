@@ -1,8 +1,40 @@
 // Memory-bound kernels of the encoder: patch gather, per-token metadata,
 // rotary table, zero fill and LayerNorm.  All written for wave64 (gfx950).
+#include <mutex>
+
+#include "../../include/qv.h"
 #include "qv_internal.h"
 
 namespace qv {
+
+// ------------------------------------------------------------------ scratch
+// Workspace of qv_vision_forward_noalloc: one copy per GPU, allocated by the
+// loader with the code object and held until the process ends.  Host code
+// never passes `scratch` itself to a kernel (on the host that name is a
+// stand-in, not a device address): scratch_buffer() resolves the device
+// address once per device with hipGetSymbolAddress and every launch takes
+// that pointer, exactly as it takes a caller's workspace.
+static __device__ __align__(256) unsigned char scratch[QV_SCRATCH_BYTES];
+
+hipError_t scratch_buffer(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> g(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p || (reinterpret_cast<uintptr_t>(p) & 255)) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 // float -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }

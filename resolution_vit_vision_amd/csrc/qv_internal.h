@@ -105,6 +105,10 @@ hipError_t launch_setup_plan(const PlanEntry* host_plan_chunk, int count, int fi
 hipError_t launch_rope_table(float2* tab, int positions, float theta, hipStream_t s);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 
+// Static device workspace of the allocation-free forward: its device address
+// on the current device (looked up once per device, then cached).
+hipError_t scratch_buffer(void** ptr);
+
 hipError_t launch_layernorm(const float* x, const float* g, const float* b, void* y, bool bf16, int rows,
                             int dim, float eps, hipStream_t s);
 

@@ -254,6 +254,18 @@ def vision_forward(cfg: VisionConfig, w: VisionWeights, patches: torch.Tensor, g
     return hidden
 
 
+def vision_forward_noalloc(cfg: VisionConfig, w: VisionWeights, patches: torch.Tensor, grids,
+                           cu_seqlens: torch.Tensor, hidden: torch.Tensor, stream=None) -> torch.Tensor:
+    """qv_vision_forward_noalloc: the same forward with the library's static
+    device workspace (no allocation by the library or here; `hidden` is the
+    caller's)."""
+    g = _grid_array(grids)
+    c = cfg.c()
+    check(lib().qv_vision_forward_noalloc(ctypes.byref(c), ctypes.byref(w.struct), _ptr(patches), g.ctypes.data,
+                                          len(g), _ptr(cu_seqlens), _ptr(hidden), _stream(stream)))
+    return hidden
+
+
 def merge_workspace_size(cfg: MergerConfig, n_tokens: int) -> int:
     n = ctypes.c_size_t()
     check(lib().qv_merge_workspace_size(ctypes.byref(cfg.c()), n_tokens, ctypes.byref(n)))

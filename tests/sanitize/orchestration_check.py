@@ -48,7 +48,10 @@ def main() -> int:
             w = _abi.VisionW(0x40000, None, blocks)
             _abi.check(L.qv_vision_forward(ctypes.byref(c), ctypes.byref(w), dev, g.ctypes.data, len(g), dev, dev,
                                            ws, nbytes.value, None))
-            runs += 1
+            st = L.qv_vision_forward_noalloc(ctypes.byref(c), ctypes.byref(w), dev, g.ctypes.data, len(g), dev, dev,
+                                             None)
+            assert st == (_abi.QV_OK if nbytes.value <= _abi.QV_SCRATCH_BYTES else _abi.QV_ERR_WORKSPACE), st
+            runs += 2
         n = int((g[:, 0].astype(np.int64) * g[:, 1] * g[:, 2]).sum())
         mc = MergerConfig(out_dim=wl.out_dim, dtype=wl.dtype).c()
         mb = ctypes.c_size_t()

@@ -17,7 +17,7 @@ def test_library_exports_every_header_symbol():
     assert len(names) >= 10
     missing = [n for n in names if not hasattr(L, n)]
     assert not missing, missing
-    assert L.qv_abi_version() == 3
+    assert L.qv_abi_version() == 4
 
 
 def test_grid_params_default():
