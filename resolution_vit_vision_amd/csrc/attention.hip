@@ -376,7 +376,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
   constexpr int NST = 4;
   constexpr int BLKS = (K_BYTES + V_BYTES) / 1024;  // 10 DMA blocks per stage
   constexpr int LWMAX = (BLKS + NW - 1) / NW;
-  __shared__ __attribute__((aligned(1024))) char lds[NST * STRIDE];
+  // one LDS object for the ring and the redo flags (NW ints past the ring):
+  // a second __shared__ array makes the compiler wait for every LDS-DMA
+  // load before each LDS read, which empties the ring
+  __shared__ __attribute__((aligned(1024))) char lds[NST * STRIDE + 4 * NW];
+  int* const redo_flag = reinterpret_cast<int*>(lds + NST * STRIDE);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -461,27 +465,27 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
   }
 
   const int iters = (n + IK - 1) / IK;
-  QV_L_ISSUE(0, 0)
   bf16x8 qf[5];
-  {
-    const uint16_t* qr = Qh + (size_t)(pe.prow0 + qbase + l32) * kHeadDim + 8 * hlf;
-#pragma unroll
-    for (int kk = 0; kk < 5; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qr + 16 * kk);
+
+  // Ring prologue: stages 0..2 in flight, this wave's q fragments, the
+  // constant block (eight bf16 ones, eight zeros) of every stage.
+#define QV_L_PROLOGUE()                                                                                      \
+  {                                                                                                          \
+    QV_L_ISSUE(0, 0)                                                                                         \
+    const uint16_t* qr = Qh + (size_t)(pe.prow0 + qbase + l32) * kHeadDim + 8 * hlf;                         \
+    _Pragma("unroll") for (int kk = 0; kk < 5; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qr + 16 * kk); \
+    if (wave == 0 && lane < 2 * NST) {                                                                       \
+      const uint32_t w = (lane & 1) ? 0u : 0x3F803F80u;                                                      \
+      *reinterpret_cast<uint4*>(lds + (lane >> 1) * STRIDE + CONST_OFF + 16 * (lane & 1)) =                  \
+          make_uint4(w, w, w, w);                                                                            \
+    }                                                                                                        \
+    QV_WAIT_VM(0);                                                                                           \
+    __syncthreads();                                                                                         \
+    if (iters > 1) QV_L_ISSUE(1, 1)                                                                          \
+    if (iters > 2) QV_L_ISSUE(2, 2)                                                                          \
   }
-  if (wave == 0 && lane < 2 * NST) {
-    const uint32_t w = (lane & 1) ? 0u : 0x3F803F80u;
-    *reinterpret_cast<uint4*>(lds + (lane >> 1) * STRIDE + CONST_OFF + 16 * (lane & 1)) = make_uint4(w, w, w, w);
-  }
-  QV_WAIT_VM(0);
-  __syncthreads();
-  if (iters > 1) QV_L_ISSUE(1, 1)
-  if (iters > 2) QV_L_ISSUE(2, 2)
 
   f32x16 o[3];
-#pragma unroll
-  for (int t = 0; t < 3; ++t)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
 
 #define QV_L_S(ST, SACC)                                                                                     \
   {                                                                                                          \
@@ -513,17 +517,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
   // argument leaves the matrix core ready for v_exp_f32.
   f32x16 s_cur, s_nxt, negm;
   float m_run;
-  QV_L_S(0, s_cur)
-  QV_L_MASK(0, s_cur)
-  QV_L_MAX(s_cur, m_run)
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    s_cur[r] -= m_run;
-    negm[r] = -m_run;
+#define QV_L_FIRST()                                                                                         \
+  {                                                                                                          \
+    _Pragma("unroll") for (int t = 0; t < 3; ++t)                                                            \
+    _Pragma("unroll") for (int r = 0; r < 16; ++r) o[t][r] = 0.f;                                           \
+    QV_L_S(0, s_cur)                                                                                         \
+    QV_L_MASK(0, s_cur)                                                                                      \
+    QV_L_MAX(s_cur, m_run)                                                                                   \
+    _Pragma("unroll") for (int r = 0; r < 16; ++r) {                                                         \
+      s_cur[r] -= m_run;                                                                                     \
+      negm[r] = -m_run;                                                                                      \
+    }                                                                                                        \
   }
 
-  // one step: tile IT in stage ST (compile-time)
-#define QV_L_STEP(IT, ST)                                                                                    \
+  // one step: tile IT in stage ST (compile-time).  LAZY (compile-time): the
+  // next tile's max is taken and the reference moves when a score exceeds
+  // it by more than 2^kLazyLog2; otherwise the reference stays at the first
+  // tile's maximum for the whole row.
+#define QV_L_STEP(IT, ST, LAZY)                                                                              \
   {                                                                                                          \
     const bool more_ = (IT) + 1 < iters;                                                                     \
     if (more_) {                                                                                             \
@@ -567,8 +578,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
       o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf_[t], pb[0], o[t], 0, 0, 0);                          \
     _Pragma("unroll") for (int e = 0; e < 8; ++e)                                                            \
       pb[1][e] = (__bf16)__builtin_amdgcn_exp2f(s_cur[8 + e]);                                               \
-    float cand_;                                                                                             \
-    QV_L_MAX(s_nxt, cand_)                                                                                   \
+    float cand_ = 0.f;                                                                                       \
+    if (LAZY) QV_L_MAX(s_nxt, cand_)                                                                         \
     _Pragma("unroll") for (int t = 0; t < 3; ++t)                                                            \
       o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf_[3 + t], pb[1], o[t], 0, 0, 0);                      \
     {                                                                                                        \
@@ -581,31 +592,65 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
         __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);                                                   \
       }                                                                                                      \
     }                                                                                                        \
-    const bool grow_ = more_ && cand_ > kLazyLog2;                                                           \
-    if (__any(grow_)) {                                                                                      \
-      const float d_ = grow_ ? cand_ : 0.f;                                                                  \
-      const float alpha_ = __builtin_amdgcn_exp2f(-d_);                                                      \
-      m_run += d_;                                                                                           \
-      _Pragma("unroll") for (int t = 0; t < 3; ++t)                                                         \
-      _Pragma("unroll") for (int r = 0; r < 16; ++r) o[t][r] *= alpha_;                                     \
-      _Pragma("unroll") for (int r = 0; r < 16; ++r) {                                                      \
-        s_nxt[r] -= d_;                                                                                      \
-        negm[r] = -m_run;                                                                                    \
+    if (LAZY) {                                                                                              \
+      const bool grow_ = more_ && cand_ > kLazyLog2;                                                         \
+      if (__any(grow_)) {                                                                                    \
+        const float d_ = grow_ ? cand_ : 0.f;                                                                \
+        const float alpha_ = __builtin_amdgcn_exp2f(-d_);                                                    \
+        m_run += d_;                                                                                         \
+        _Pragma("unroll") for (int t = 0; t < 3; ++t)                                                       \
+        _Pragma("unroll") for (int r = 0; r < 16; ++r) o[t][r] *= alpha_;                                   \
+        _Pragma("unroll") for (int r = 0; r < 16; ++r) {                                                    \
+          s_nxt[r] -= d_;                                                                                    \
+          negm[r] = -m_run;                                                                                  \
+        }                                                                                                    \
       }                                                                                                      \
     }                                                                                                        \
     s_cur = s_nxt;                                                                                           \
   }
-
-  for (int it = 0; it < iters; it += NST) {
-    QV_L_STEP(it, 0)
-    if (it + 1 >= iters) break;
-    QV_L_STEP(it + 1, 1)
-    if (it + 2 >= iters) break;
-    QV_L_STEP(it + 2, 2)
-    if (it + 3 >= iters) break;
-    QV_L_STEP(it + 3, 3)
+#define QV_L_LOOP(LAZY)                                                                                      \
+  for (int it = 0; it < iters; it += NST) {                                                                  \
+    QV_L_STEP(it, 0, LAZY)                                                                                   \
+    if (it + 1 >= iters) break;                                                                              \
+    QV_L_STEP(it + 1, 1, LAZY)                                                                               \
+    if (it + 2 >= iters) break;                                                                              \
+    QV_L_STEP(it + 2, 2, LAZY)                                                                               \
+    if (it + 3 >= iters) break;                                                                              \
+    QV_L_STEP(it + 3, 3, LAZY)                                                                               \
   }
+
+  // Fast pass: the reference stays at the first key tile's maximum, so a
+  // step needs no max and no rescale.  Exact up to rounding as long as no
+  // exponent overflows: a score above the reference by 128 (log2 units) or
+  // a sum past the float range shows up as inf / NaN in the accumulators,
+  // and then the whole workgroup runs the rows again with the lazy running
+  // maximum, which bounds every exponent.
+  QV_L_PROLOGUE()
+  QV_L_FIRST()
+  QV_L_LOOP(false)
+  {
+    float chk = 0.f;
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) chk += o[t][r];
+    const int bad = __any(!__builtin_isfinite(chk)) ? 1 : 0;  // every lane votes (not inside the lane-0 branch)
+    if (lane == 0) redo_flag[wave] = bad;
+    __syncthreads();
+    int redo = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) redo |= redo_flag[w];
+    if (redo) {
+      __syncthreads();  // every wave has read the flags and finished with the ring
+      QV_L_PROLOGUE()
+      QV_L_FIRST()
+      QV_L_LOOP(true)
+    }
+  }
+#undef QV_L_LOOP
 #undef QV_L_STEP
+#undef QV_L_FIRST
+#undef QV_L_PROLOGUE
 #undef QV_L_S
 #undef QV_L_MASK
 #undef QV_L_MAX

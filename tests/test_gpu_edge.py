@@ -116,3 +116,55 @@ def test_inconsistent_cu_seqlens_is_harmless_and_flagged():
         del os.environ["QV_DEBUG_VALIDATE"]
         enc.cu.copy_(good)
         torch.cuda.synchronize()
+
+
+def test_long_attention_overflow_redoes_with_running_max():
+    """The long-sequence attention kernel first keeps the softmax reference
+    at the first key tile's maximum; a score above it by more than the float
+    exponent range turns its accumulators to inf, and the workgroup must
+    redo its rows with the running maximum.  One patch of a 64x64 grid
+    (4096 patches, past the first key tile) carries a spike that LayerNorm
+    turns into a huge key component, and head 0's query bias makes its score
+    up to about 370 (log2 units, times the cosine of the rotary offset
+    between the two rows) while first-tile scores stay below about 30: the
+    head-0 rows near that patch's row of the grid overflow and attend to it
+    alone.  The block's update (output minus input) must match the
+    oracle's."""
+    qv = _qv()
+    from resolution_vit_vision_amd.encoder import VisionConfig, VisionWeights
+    rng = np.random.default_rng(41)
+    d, m, n = 1280, 5120, 4096
+    grids = [(1, 64, 64)]
+    cu, pos, _ = O.seq_meta(grids)
+    bf = lambda a: synth.round_bf16(np.asarray(a, dtype=np.float32)).astype(np.float64)
+    x = bf(rng.standard_normal((n, 1176)))
+    x[100, 0] = 2000.0                              # the spiked patch (row 100: past keys 0..31)
+    pw = np.zeros((d, 3, 2, 14, 14))
+    pw.reshape(d, 1176)[np.arange(1176), np.arange(1176)] = 1.0
+    p = {"patch_w": pw}
+    blk = {"ln1_w": np.ones(d), "ln1_b": np.zeros(d),
+           "qkv_w": np.zeros((3 * d, d)), "qkv_b": np.zeros(3 * d),
+           "proj_w": bf(0.02 * rng.standard_normal((d, d))), "proj_b": bf(0.02 * rng.standard_normal(d)),
+           "ln2_w": np.ones(d), "ln2_b": np.zeros(d),
+           "fc1_w": bf(0.02 * rng.standard_normal((m, d))), "fc1_b": bf(0.02 * rng.standard_normal(m)),
+           "fc2_w": bf(0.02 * rng.standard_normal((d, m))), "fc2_b": bf(0.02 * rng.standard_normal(d))}
+    blk["qkv_b"][0] = 64.0                          # head 0, q element 0
+    blk["qkv_w"][d + 0, 0] = 1.0                    # head 0, k element 0 reads LN1(z)[0]
+    blk["qkv_w"][2 * d:] = bf(0.02 * rng.standard_normal((d, d)))
+    for k, v in blk.items():
+        p["blocks.0." + k] = v
+    cfg = VisionConfig(depth=1, patch_dim=1176, ld=1176)
+    w = VisionWeights(p, 1, "bf16")
+    patches = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).cuda()
+    cu_d = torch.from_numpy(cu.astype(np.int32)).cuda()
+    _say("long attention overflow: 64x64 grid, one spiked key, depth 1")
+    hid = qv.vision_forward(cfg, w, patches, grids, cu_d)
+    torch.cuda.synchronize()
+    got = hid.cpu().double().numpy()
+    assert np.isfinite(got).all()
+    z = x @ pw.reshape(d, 1176).T                  # exact on the GPU too (identity weight, bf16 patches)
+    ref = O.vision_block(z, O.block_params(p, 0), cu, O.rope_angles(pos))
+    # the block's own contribution: the residual stream would hide it
+    e = rel_l2(got - z, ref - z)
+    _say(f"  block update rel-L2 {e:.3e}")
+    assert e <= 2e-2
