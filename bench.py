@@ -121,7 +121,7 @@ def cpu_baseline(wl, params, imgs):
             "seconds": dt, "passes": passes, "blas_threads": blas_threads, "affinity_cores": cores}
 
 
-def cpu_baseline_extrapolated(wl, params, imgs, rows=(1024, 4096), merge_groups=1024):
+def cpu_baseline_extrapolated(wl, params, imgs, rows=(2048, 8192), merge_groups=2048):
     """The oracle (float32 mode) timed on a bounded sample of a workload too
     large to run whole, scaled to the whole forward and labelled so:
     patchify + patch-embed over every patch; one full-shape block evaluated at

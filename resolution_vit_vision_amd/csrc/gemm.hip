@@ -664,7 +664,19 @@ static hipError_t run_pipe(const void* A, int lda, const void* B, int ldb, int M
   // 128 x 128 warp-specialized kernel at these sizes, so one round of them
   // on 160 or more CUs beats about three rounds of the smaller tile
   // (4 x 672x672: fc2 5.25 -> 4.24 ms per forward at 180 tiles)
-  if (t256 >= 160) return launch_pipe<256, 256, 2, 4, 2, KT>(A, lda, B, ldb, M, N, epi, rmap, s);
+  if (t256 >= 160) {
+    // 192-row tiles when they take clearly fewer rounds of the 256 CUs in
+    // units of 64 rows of work (four 672x672 images: the q/k/v projection
+    // needs 3 rounds of 540 tiles of 256 rows or 3 of 720 tiles of 192; the
+    // out-projection and the MLP down-projection 1 round either way, with
+    // 180 or 240 tiles).  Measured there: q/k/v, out-projection and fc2 each
+    // 6 % faster (three quarters of the work per tile, at a lower rate per
+    // flop than the 256-row tile), the step 3.5 %; same output bits.
+    const int64_t tn = (N + 255) / 256;
+    const int64_t r256 = ((M + 255) / 256 * tn + 255) / 256, r192 = ((M + 191) / 192 * tn + 255) / 256;
+    if (10 * 3 * r192 <= 9 * 4 * r256) return launch_pipe<192, 256, 2, 4, 2, KT>(A, lda, B, ldb, M, N, epi, rmap, s);
+    return launch_pipe<256, 256, 2, 4, 2, KT>(A, lda, B, ldb, M, N, epi, rmap, s);
+  }
   if constexpr (ALLOW160)
     if (N % 160 == 0 && t160 >= 192 && t160 <= 256)
       return launch_ws<128, 160, 4, 1, 4, KT, 4>(A, lda, B, ldb, M, N, epi, rmap, s);
