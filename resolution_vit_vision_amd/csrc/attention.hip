@@ -533,7 +533,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
   // one step: tile IT in stage ST (compile-time).  LAZY (compile-time): the
   // next tile's max is taken and the reference moves when a score exceeds
   // it by more than 2^kLazyLog2; otherwise the reference stays at the first
-  // tile's maximum for the whole row.
+  // tile's maximum for the whole row.  Without the max the step's 24 VALU
+  // instructions (16 exponentials, 8 packs) go two beside each of its 11
+  // MFMAs (4 x 672x672: attention 133 -> 126 us against the schedule tuned
+  // for the lazy step).
 #define QV_L_STEP(IT, ST, LAZY)                                                                              \
   {                                                                                                          \
     const bool more_ = (IT) + 1 < iters;                                                                     \
@@ -561,7 +564,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
       vf_[3 * s2 + t] = *reinterpret_cast<const bf16x8*>(lds + (ST) * STRIDE +                               \
                                                        (t < 2 ? voff[s2] + t * 2048 : voff2[s2]));           \
     asm volatile("" ::"v"(pb[0]));                                                                           \
-    {                                                                                                        \
+    if (LAZY) {                                                                                              \
       __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);                                                     \
       __builtin_amdgcn_sched_group_barrier(0x402, 3, 0);                                                     \
       _Pragma("unroll") for (int g_ = 0; g_ < 3; ++g_) {                                                     \
@@ -571,6 +574,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                     \
       __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);                                                     \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                     \
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);                                                     \
+    } else {                                                                                                 \
+      __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);                                                     \
+      __builtin_amdgcn_sched_group_barrier(0x402, 2, 0);                                                     \
+      _Pragma("unroll") for (int g_ = 0; g_ < 5; ++g_) {                                                     \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                   \
+        __builtin_amdgcn_sched_group_barrier(0x402, 2, 0);                                                   \
+      }                                                                                                      \
       __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);                                                     \
     }                                                                                                        \
     if (more_) QV_L_MASK((IT) + 1, s_nxt)                                                                    \
@@ -582,7 +593,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
     if (LAZY) QV_L_MAX(s_nxt, cand_)                                                                         \
     _Pragma("unroll") for (int t = 0; t < 3; ++t)                                                            \
       o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf_[3 + t], pb[1], o[t], 0, 0, 0);                      \
-    {                                                                                                        \
+    if (LAZY) {                                                                                              \
       _Pragma("unroll") for (int g_ = 0; g_ < 3; ++g_) {                                                     \
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                   \
         __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);                                                   \
@@ -590,6 +601,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
       _Pragma("unroll") for (int g_ = 0; g_ < 3; ++g_) {                                                     \
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                   \
         __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);                                                   \
+      }                                                                                                      \
+    } else {                                                                                                 \
+      _Pragma("unroll") for (int g_ = 0; g_ < 6; ++g_) {                                                     \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                   \
+        __builtin_amdgcn_sched_group_barrier(0x402, 2, 0);                                                   \
       }                                                                                                      \
     }                                                                                                        \
     if (LAZY) {                                                                                              \
