@@ -665,16 +665,24 @@ static hipError_t run_pipe(const void* A, int lda, const void* B, int ldb, int M
   // on 160 or more CUs beats about three rounds of the smaller tile
   // (4 x 672x672: fc2 5.25 -> 4.24 ms per forward at 180 tiles)
   if (t256 >= 160) {
-    // 192-row tiles when they take clearly fewer rounds of the 256 CUs in
-    // units of 64 rows of work (four 672x672 images: the q/k/v projection
-    // needs 3 rounds of 540 tiles of 256 rows or 3 of 720 tiles of 192; the
-    // out-projection and the MLP down-projection 1 round either way, with
-    // 180 or 240 tiles).  Measured there: q/k/v, out-projection and fc2 each
-    // 6 % faster (three quarters of the work per tile, at a lower rate per
-    // flop than the 256-row tile), the step 3.5 %; same output bits.
+    // Tile height 192, 256 or 320 rows (256 columns, 8 waves, 2 stages):
+    // the one with the least rounds x rows x relative cost per flop, the
+    // rounds counted over the 256 CUs.  Per-flop costs 1.25 / 1.00 / 0.96
+    // are measured (a 192-row tile does 75 % of the work of a 256-row one in
+    // 94 % of the time; a 320-row one 125 % in 120 %).  Measured choices:
+    // four 672x672 images take 320 rows for q/k/v (108.6 against 113.1 us
+    // with 192), 192 for the out-projection and fc2, 256 for fc1; the mixed
+    // 16-image batch takes 320 everywhere (fc2 590 -> 530 us, fc1 520 ->
+    // 492, step -4.5 %); 3584x3584 keeps 256.  Output bits do not depend on
+    // the tiling.
     const int64_t tn = (N + 255) / 256;
-    const int64_t r256 = ((M + 255) / 256 * tn + 255) / 256, r192 = ((M + 191) / 192 * tn + 255) / 256;
-    if (10 * 3 * r192 <= 9 * 4 * r256) return launch_pipe<192, 256, 2, 4, 2, KT>(A, lda, B, ldb, M, N, epi, rmap, s);
+    auto cost = [&](int bm, int64_t per_flop) {
+      const int64_t rounds = ((M + bm - 1) / bm * tn + 255) / 256;
+      return rounds * bm * per_flop;
+    };
+    const int64_t c192 = cost(192, 125), c256 = cost(256, 100), c320 = cost(320, 96);
+    if (c192 < c256 && c192 <= c320) return launch_pipe<192, 256, 2, 4, 2, KT>(A, lda, B, ldb, M, N, epi, rmap, s);
+    if (c320 < c256) return launch_pipe<320, 256, 2, 4, 2, KT>(A, lda, B, ldb, M, N, epi, rmap, s);
     return launch_pipe<256, 256, 2, 4, 2, KT>(A, lda, B, ldb, M, N, epi, rmap, s);
   }
   if constexpr (ALLOW160)
