@@ -52,46 +52,90 @@ __device__ __forceinline__ float act_apply(Act a, float u) {
 // e.g. the residual) and store(row, col, v[VEC], rp).
 struct NoRowParam {};
 
+// Epilogue operands that do not depend on the accumulators (per-column bias,
+// residual rows, token info, rotary entries) are loaded by the epilogue's
+// prefetch() before the K loop when they fit in a few registers, so their
+// memory latency hides under the main loop instead of opening the epilogue
+// (measured: 0.7-1.1 us per GEMM at 1024 rows, 20-60 us per GEMM at 65,536).
+// Where they do not fit, the next 32-row block's row values are loaded while
+// the current block is staged and stored.  prefetch(..., active = false)
+// loads nothing (waves that leave before the epilogue).
 template <int VEC, class Op, int FM, int FN>
-__device__ __forceinline__ void staged_store(const Op& op, f32x16 (&acc)[FM][FN], float* wlds, int wm0, int wn0,
-                                             int lane, int M, int N) {
-  constexpr int LD = 40;
-  constexpr int LPR = 32 / VEC;          // lanes per 32-column row
-  constexpr int RPP = 64 / LPR;          // rows per pass
-  constexpr int PASSES = 32 / RPP;
+struct StagedPre {
+  static constexpr int LPR = 32 / VEC;   // lanes per 32-column row
+  static constexpr int RPP = 64 / LPR;   // rows per pass
+  static constexpr int PASSES = 32 / RPP;
+  static constexpr bool HAS_RP = Op::kRowParamFloats > 0;
+  // every row value of the wave tile in at most 64 registers: all of them up front
+  static constexpr bool ALL = HAS_RP && FM * FN * PASSES * Op::kRowParamFloats <= 64;
+  // otherwise one block ahead, where two blocks' values leave the tile's
+  // accumulators enough registers
+  static constexpr bool AHEAD = HAS_RP && !ALL && FM <= 4;
+  // and the first block's before the K loop when it takes at most 32 registers
+  static constexpr bool FIRST = AHEAD && FN * PASSES * Op::kRowParamFloats <= 32;
   using RP = typename Op::RowParam;
   float cp[FN];
+  RP rp[ALL ? FM : 1][FN][PASSES];   // AHEAD: the first block's
+};
+
+template <int VEC, class Op, int FM, int FN>
+__device__ __forceinline__ void staged_rows(const Op& op, typename Op::RowParam (&dst)[FN][32 / (64 / (32 / VEC))],
+                                            int rb, int wn0, int lane, int M, int N) {
+  constexpr int LPR = 32 / VEC, RPP = 64 / LPR, PASSES = 32 / RPP;
+  const int rl0 = lane / LPR, cl = (lane % LPR) * VEC;
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+    for (int pass = 0; pass < PASSES; ++pass) {
+      const int row = rb + pass * RPP + rl0, col = wn0 + fn * 32 + cl;
+      if (row < M && col < N) dst[fn][pass] = op.row_param(row, col);
+    }
+}
+
+template <int VEC, class Op, int FM, int FN>
+__device__ __forceinline__ StagedPre<VEC, Op, FM, FN> staged_prefetch(const Op& op, int wm0, int wn0, int lane, int M,
+                                                                      int N, bool active) {
+  using P = StagedPre<VEC, Op, FM, FN>;
+  P p;
+  if (!active) return p;
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn) {
     const int col = wn0 + fn * 32 + (lane & 31);
-    cp[fn] = col < N ? op.col_param(col) : 0.f;
+    p.cp[fn] = col < N ? op.col_param(col) : 0.f;
   }
+  if constexpr (P::ALL) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) staged_rows<VEC, Op, FM, FN>(op, p.rp[fm], wm0 + fm * 32, wn0, lane, M, N);
+  } else if constexpr (P::FIRST) {
+    staged_rows<VEC, Op, FM, FN>(op, p.rp[0], wm0, wn0, lane, M, N);
+  }
+  return p;
+}
+
+template <int VEC, class Op, int FM, int FN>
+__device__ __forceinline__ void staged_store(const Op& op, f32x16 (&acc)[FM][FN], float* wlds, int wm0, int wn0,
+                                             int lane, int M, int N, const StagedPre<VEC, Op, FM, FN>& pre) {
+  using P = StagedPre<VEC, Op, FM, FN>;
+  using RP = typename Op::RowParam;
+  constexpr int LD = 40;
+  constexpr int LPR = P::LPR, RPP = P::RPP, PASSES = P::PASSES;
   const int rl0 = lane / LPR, cl = (lane % LPR) * VEC;
-  // residual-style row params: all of them up front when they fit in 64
-  // registers, otherwise one 32-row block at a time
-  constexpr bool ALL = FM * FN * PASSES * Op::kRowParamFloats <= 64;
-  RP rp[ALL ? FM : 1][FN][PASSES];
-  if constexpr (Op::kRowParamFloats > 0 && ALL) {
+  RP rq[P::AHEAD ? 2 : 1][FN][PASSES];
+  if constexpr (P::FIRST) {
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
+    for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-        for (int pass = 0; pass < PASSES; ++pass) {
-          const int row = wm0 + fm * 32 + pass * RPP + rl0, col = wn0 + fn * 32 + cl;
-          if (row < M && col < N) rp[fm][fn][pass] = op.row_param(row, col);
-        }
+      for (int pass = 0; pass < PASSES; ++pass) rq[0][fn][pass] = pre.rp[0][fn][pass];
+  } else if constexpr (P::HAS_RP && !P::ALL) {
+    staged_rows<VEC, Op, FM, FN>(op, rq[0], wm0, wn0, lane, M, N);
   }
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
-    if constexpr (Op::kRowParamFloats > 0 && !ALL) {
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-        for (int pass = 0; pass < PASSES; ++pass) {
-          const int row = wm0 + fm * 32 + pass * RPP + rl0, col = wn0 + fn * 32 + cl;
-          if (row < M && col < N) rp[0][fn][pass] = op.row_param(row, col);
-        }
+    // row values of the next block, issued before this block's first store
+    if constexpr (P::AHEAD) {
+      if (fm + 1 < FM) staged_rows<VEC, Op, FM, FN>(op, rq[(fm + 1) & 1], wm0 + (fm + 1) * 32, wn0, lane, M, N);
+    } else if constexpr (P::HAS_RP && !P::ALL) {
+      if (fm > 0) staged_rows<VEC, Op, FM, FN>(op, rq[0], wm0 + fm * 32, wn0, lane, M, N);
     }
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
@@ -99,7 +143,7 @@ __device__ __forceinline__ void staged_store(const Op& op, f32x16 (&acc)[FM][FN]
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int rl = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        wlds[rl * LD + (lane & 31)] = op.pre(cp[fn], acc[fm][fn][r]);
+        wlds[rl * LD + (lane & 31)] = op.pre(pre.cp[fn], acc[fm][fn][r]);
       }
 #pragma unroll
       for (int pass = 0; pass < PASSES; ++pass) {
@@ -111,11 +155,27 @@ __device__ __forceinline__ void staged_store(const Op& op, f32x16 (&acc)[FM][FN]
           v[q] = t.x; v[q + 1] = t.y; v[q + 2] = t.z; v[q + 3] = t.w;
         }
         const int row = wm0 + fm * 32 + rl, col = col0 + cl;
-        if (row < M && col < N) op.store(row, col, v, rp[ALL ? fm : 0][fn][pass]);
+        const RP& rp = P::ALL ? pre.rp[P::ALL ? fm : 0][fn][pass] : rq[P::AHEAD ? (fm & 1) : 0][fn][pass];
+        if (row < M && col < N) op.store(row, col, v, rp);
       }
     }
   }
 }
+
+// The prefetch / apply pair of an epilogue whose values go through
+// staged_store with VEC columns per lane.
+#define QV_STAGED_EPILOGUE(SELF, VEC)                                                                          \
+  template <int FM, int FN>                                                                                    \
+  using Pre = StagedPre<VEC, SELF, FM, FN>;                                                                    \
+  template <int FM, int FN, bool DEEP>                                                                         \
+  __device__ __forceinline__ Pre<FM, FN> prefetch(int wm0, int wn0, int lane, int M, int N, bool active) const { \
+    return staged_prefetch<VEC, SELF, FM, FN>(*this, wm0, wn0, lane, M, N, active);                            \
+  }                                                                                                            \
+  template <int FM, int FN>                                                                                    \
+  __device__ __forceinline__ void apply_staged(f32x16 (&acc)[FM][FN], float* wlds, int wm0, int wn0, int lane,  \
+                                               int M, int N, const Pre<FM, FN>& pre) const {                   \
+    staged_store<VEC>(*this, acc, wlds, wm0, wn0, lane, M, N, pre);                                            \
+  }
 
 // QuickGELU for the bf16 path with a hardware reciprocal (1 ulp; the result
 // is rounded to bf16).
@@ -137,10 +197,7 @@ struct EpiStoreF32 {
   __device__ void store(int row, int col, const float (&v)[4], const RowParam&) const {
     *reinterpret_cast<float4*>(C + (size_t)row * ldc + col) = make_float4(v[0], v[1], v[2], v[3]);
   }
-  template <int FM, int FN>
-  __device__ __forceinline__ void apply_staged(f32x16 (&acc)[FM][FN], float* wlds, int wm0, int wn0, int lane, int M, int N) const {
-    staged_store<4>(*this, acc, wlds, wm0, wn0, lane, M, N);
-  }
+  QV_STAGED_EPILOGUE(EpiStoreF32, 4)
   template <int FM, int FN>
   __device__ void apply(f32x16 (&acc)[FM][FN], int wm0, int wn0, int lane, int M, int N) const {
 #pragma unroll
@@ -174,10 +231,7 @@ struct EpiPartF32 {
   __device__ void store(int row, int col, const float (&v)[4], const RowParam&) const {
     *reinterpret_cast<float4*>(C + (size_t)row * ldc + col) = make_float4(v[0], v[1], v[2], v[3]);
   }
-  template <int FM, int FN>
-  __device__ __forceinline__ void apply_staged(f32x16 (&acc)[FM][FN], float* wlds, int wm0, int wn0, int lane, int M, int N) const {
-    staged_store<4>(*this, acc, wlds, wm0, wn0, lane, M, N);
-  }
+  QV_STAGED_EPILOGUE(EpiPartF32, 4)
 };
 
 __device__ __forceinline__ EpiPartF32 epi_at_split(const EpiPartF32& e, int s) {
@@ -201,10 +255,7 @@ struct EpiResidF32 {
     *reinterpret_cast<float4*>(Z + (size_t)row * ldz + col) =
         make_float4(z.x + v[0], z.y + v[1], z.z + v[2], z.w + v[3]);
   }
-  template <int FM, int FN>
-  __device__ __forceinline__ void apply_staged(f32x16 (&acc)[FM][FN], float* wlds, int wm0, int wn0, int lane, int M, int N) const {
-    staged_store<4>(*this, acc, wlds, wm0, wn0, lane, M, N);
-  }
+  QV_STAGED_EPILOGUE(EpiResidF32, 4)
   template <int FM, int FN>
   __device__ void apply(f32x16 (&acc)[FM][FN], int wm0, int wn0, int lane, int M, int N) const {
 #pragma unroll
@@ -246,10 +297,7 @@ struct EpiActBf16 {
     pk.w = pack_bf16(v[6], v[7]);
     *reinterpret_cast<uint4*>(C + (size_t)row * ldc + col) = pk;
   }
-  template <int FM, int FN>
-  __device__ __forceinline__ void apply_staged(f32x16 (&acc)[FM][FN], float* wlds, int wm0, int wn0, int lane, int M, int N) const {
-    staged_store<8>(*this, acc, wlds, wm0, wn0, lane, M, N);
-  }
+  QV_STAGED_EPILOGUE(EpiActBf16, 8)
   template <int FM, int FN>
   __device__ void apply(f32x16 (&acc)[FM][FN], int wm0, int wn0, int lane, int M, int N) const {
 #pragma unroll
@@ -295,6 +343,21 @@ struct RowMapQkv {
   __device__ int operator()(int r) const { return qkv_weight_row(r, dim); }
 };
 
+// The rotation of a pair (x0, x1) by the angle with cs = (cos, sin), in
+// explicitly fused forms: x0 cos - x1 sin and x1 cos + x0 sin each round one
+// product and fuse the other, so the result does not depend on which
+// product the compiler would contract in a given code layout.
+__device__ __forceinline__ float rot0(float x0, float x1, float2 cs) {
+#pragma clang fp contract(off)
+  const float t = x1 * cs.y;
+  return __builtin_fmaf(x0, cs.x, -t);
+}
+__device__ __forceinline__ float rot1(float x0, float x1, float2 cs) {
+#pragma clang fp contract(off)
+  const float t = x0 * cs.y;
+  return __builtin_fmaf(x1, cs.x, t);
+}
+
 // q leaves the projection multiplied by log2(e)/sqrt(80), so the attention
 // kernels' scores are already the exponent in base 2.
 constexpr float kQScaleLog2 = 0.16129820911147802f;
@@ -304,58 +367,141 @@ struct EpiQkv {
   static constexpr int kPatchFloats = 32 * 72;  // q/k: 32 rows x (64 + 8) floats
   QkvOut o; const float* bias;
 
+  // Values that do not depend on the accumulators, loaded before the K loop
+  // (see staged_prefetch).  q/k waves: the bias of their rotation pairs and
+  // the token info of the first 32-row block; with DEEP (waves that issue no
+  // ring loads, so a dependent load costs the main loop nothing) and one
+  // block per wave, that block's rotary entries too.  v waves: the bias and
+  // every block's padded rows.
+  template <int FM, int FN>
+  struct Pre {
+    static constexpr int NP = FN / 2 > 0 ? FN / 2 : 1;
+    static constexpr bool TOK0 = FM <= 4;
+    float b0[NP], b1[NP];
+    int pos[16], prow[4];
+    float2 cs[NP][16];
+    float bb[FN];
+    int pr[FM];
+    bool has_cs;  // cs holds the first block's rotary entries (a constant once inlined)
+  };
+
+  // Rotation-pair geometry of 64-column group fp of a q/k wave tile.
+  __device__ __forceinline__ void pair_at(int v0, int c, int& f0, int& fi, int& j, int& g) const {
+    const int dim = o.dim;
+    const int region = v0 >= dim ? 1 : 0;
+    g = (v0 - region * dim) >> 6;
+    const int pair = 32 * g + c;
+    const int head = pair / (kHeadDim / 2);
+    j = pair % (kHeadDim / 2);
+    f0 = region * dim + head * kHeadDim + j;
+    fi = j < kRopeFreqs ? j : j - kRopeFreqs;
+  }
+  __device__ __forceinline__ void load_tok(int rb, int lane, int M, int (&pos)[16], int (&prow)[4]) const {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = rb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      pos[r] = row < M ? o.tokinfo[row].x : 0;
+    }
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+      const int row = rb + ((pass * 64 + lane) >> 3);
+      prow[pass] = row < M ? o.tokinfo[row].y : 0;
+    }
+  }
+  template <int NP>
+  __device__ __forceinline__ void load_cs(const int (&pos)[16], const int (&fi)[NP], const int (&jj)[NP],
+                                          float2 (&cs)[NP][16]) const {
+#pragma unroll
+    for (int fp = 0; fp < NP; ++fp)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int p = jj[fp] < kRopeFreqs ? (pos[r] & 0xFFFF) : (pos[r] >> 16);
+        cs[fp][r] = o.rope[p * kRopeFreqs + fi[fp]];
+      }
+  }
+
+  template <int FM, int FN, bool DEEP>
+  __device__ __forceinline__ Pre<FM, FN> prefetch(int wm0, int wn0, int lane, int M, int N, bool active) const {
+    using P = Pre<FM, FN>;
+    P p;
+    if (!active) return p;
+    const int c = lane & 31;
+    if (wn0 < 2 * o.dim) {
+      int fi[P::NP], jj[P::NP];
+#pragma unroll
+      for (int fp = 0; fp < P::NP; ++fp) {
+        int f0, g;
+        pair_at(wn0 + fp * 64, c, f0, fi[fp], jj[fp], g);
+        p.b0[fp] = bias[f0];
+        p.b1[fp] = bias[f0 + kHeadDim / 2];
+      }
+      if constexpr (P::TOK0) load_tok(wm0, lane, M, p.pos, p.prow);
+      p.has_cs = DEEP && FM == 1;
+      if constexpr (DEEP && FM == 1) load_cs<P::NP>(p.pos, fi, jj, p.cs);
+    } else {
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) p.bb[fn] = bias[wn0 + fn * 32 + c];
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        const int row = wm0 + fm * 32 + 4 * (lane & 7);
+        p.pr[fm] = row < M ? o.tokinfo[row].y : 0;
+      }
+    }
+    return p;
+  }
+
   // Staged: rotated q/k values of a 32-row block go to LDS as [row][half*32 + c]
   // and leave as 16-byte runs of 8 consecutive head elements (an aligned run
   // of 8 pairs never crosses a head, heads being 40 pairs); v goes to LDS
   // transposed [feature][row] and leaves as 8-byte runs of 4 consecutive keys
   // (a 4-aligned run of packed rows stays inside one image and maps to 4
   // contiguous key slots even after the bits-2/3 key permutation).
-  // As in staged_store, every global load (bias, token info, rotary table)
-  // of a 32-row block is issued before that block's first store.
+  // Every global load of a 32-row block is issued before that block's first
+  // store, and the next block's token info before this block's rotary loads.
   template <int FM, int FN>
-  __device__ __forceinline__ void apply_staged(f32x16 (&acc)[FM][FN], float* wlds, int wm0, int wn0, int lane, int M, int N) const {
+  __device__ __forceinline__ void apply_staged(f32x16 (&acc)[FM][FN], float* wlds, int wm0, int wn0, int lane, int M,
+                                               int N, const Pre<FM, FN>& pre) const {
+    using P = Pre<FM, FN>;
     const int dim = o.dim;
     const int c = lane & 31;
     if (wn0 < 2 * dim) {
       constexpr int NP = FN / 2;  // 64-column groups of rotation pairs
-      float b0[NP], b1[NP];
       int fi[NP], jj[NP], gg[NP];
 #pragma unroll
       for (int fp = 0; fp < NP; ++fp) {
-        const int v0 = wn0 + fp * 64;  // first virtual column of this 64-group
-        const int region = v0 >= dim ? 1 : 0;
-        const int g = (v0 - region * dim) >> 6;
-        const int pair = 32 * g + c;
-        const int head = pair / (kHeadDim / 2), j = pair % (kHeadDim / 2);
-        const int f0 = region * dim + head * kHeadDim + j;
-        b0[fp] = bias[f0];
-        b1[fp] = bias[f0 + kHeadDim / 2];
-        fi[fp] = j < kRopeFreqs ? j : j - kRopeFreqs;
-        jj[fp] = j;
-        gg[fp] = g;
+        int f0;
+        pair_at(wn0 + fp * 64, c, f0, fi[fp], jj[fp], gg[fp]);
+      }
+      // token info one block ahead where two blocks' worth leaves the tile's
+      // accumulators enough registers
+      constexpr bool AHEAD = FM > 1 && FM <= 4;
+      int pos[AHEAD ? 2 : 1][16], prow[AHEAD ? 2 : 1][4];
+      if constexpr (P::TOK0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pos[0][r] = pre.pos[r];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) prow[0][q] = pre.prow[q];
+      } else {
+        load_tok(wm0, lane, M, pos[0], prow[0]);
       }
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) {
         const int rb = wm0 + fm * 32;
-        int pos[16], prow[4];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = rb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          pos[r] = row < M ? o.tokinfo[row].x : 0;
-        }
-#pragma unroll
-        for (int pass = 0; pass < 4; ++pass) {
-          const int row = rb + ((pass * 64 + lane) >> 3);
-          prow[pass] = row < M ? o.tokinfo[row].y : 0;
+        const int cur = AHEAD ? (fm & 1) : 0;
+        if constexpr (AHEAD) {
+          if (fm + 1 < FM) load_tok(rb + 32, lane, M, pos[cur ^ 1], prow[cur ^ 1]);
+        } else {
+          if (fm > 0) load_tok(rb, lane, M, pos[0], prow[0]);
         }
         float2 cs[NP][16];
+        if (FM == 1 && pre.has_cs) {
 #pragma unroll
-        for (int fp = 0; fp < NP; ++fp)
+          for (int fp = 0; fp < NP; ++fp)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int p = jj[fp] < kRopeFreqs ? (pos[r] & 0xFFFF) : (pos[r] >> 16);
-            cs[fp][r] = o.rope[p * kRopeFreqs + fi[fp]];
-          }
+            for (int r = 0; r < 16; ++r) cs[fp][r] = pre.cs[fp][r];
+        } else {
+          load_cs<NP>(pos[cur], fi, jj, cs);
+        }
 #pragma unroll
         for (int fp = 0; fp < NP; ++fp) {
           const bool isk = wn0 + fp * 64 >= dim;
@@ -364,10 +510,10 @@ struct EpiQkv {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int rl = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            const float x0 = acc[fm][2 * fp][r] + b0[fp], x1 = acc[fm][2 * fp + 1][r] + b1[fp];
+            const float x0 = acc[fm][2 * fp][r] + pre.b0[fp], x1 = acc[fm][2 * fp + 1][r] + pre.b1[fp];
             const bool ok = rb + rl < M;
-            wlds[rl * 72 + c] = ok ? (x0 * cs[fp][r].x - x1 * cs[fp][r].y) * qs : 0.f;
-            wlds[rl * 72 + 32 + c] = ok ? (x1 * cs[fp][r].x + x0 * cs[fp][r].y) * qs : 0.f;
+            wlds[rl * 72 + c] = ok ? rot0(x0, x1, cs[fp][r]) * qs : 0.f;
+            wlds[rl * 72 + 32 + c] = ok ? rot1(x0, x1, cs[fp][r]) * qs : 0.f;
           }
 #pragma unroll
           for (int pass = 0; pass < 4; ++pass) {
@@ -384,8 +530,8 @@ struct EpiQkv {
               pk.z = pack_bf16(a1.x, a1.y);
               pk.w = pack_bf16(a1.z, a1.w);
               const int d0 = j0 + h * (kHeadDim / 2);  // 8 consecutive dims, one 16-byte chunk
-              const size_t off = isk ? kc_offset(hd, o.P, prow[pass], d0)
-                                     : ((size_t)hd * o.P + prow[pass]) * kHeadDim + d0;
+              const size_t off = isk ? kc_offset(hd, o.P, prow[cur][pass], d0)
+                                     : ((size_t)hd * o.P + prow[cur][pass]) * kHeadDim + d0;
               *reinterpret_cast<uint4*>(base + off) = pk;
             }
           }
@@ -393,15 +539,6 @@ struct EpiQkv {
       }
     } else {
       uint16_t* vt = reinterpret_cast<uint16_t*>(o.vt);
-      float bb[FN];
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn) bb[fn] = bias[wn0 + fn * 32 + c];
-      int pr[FM];  // padded row of this lane's 4-key run, the same in every pass
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm) {
-        const int row = wm0 + fm * 32 + 4 * (lane & 7);
-        pr[fm] = row < M ? o.tokinfo[row].y : 0;
-      }
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
         const int col0 = wn0 + fn * 32;
@@ -411,10 +548,10 @@ struct EpiQkv {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int rl = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            wlds[c * 36 + rl] = acc[fm][fn][r] + bb[fn];
+            wlds[c * 36 + rl] = acc[fm][fn][r] + pre.bb[fn];
           }
           const int row = rb + 4 * (lane & 7);
-          const int pp = (pr[fm] & ~12) | ((pr[fm] & 4) << 1) | ((pr[fm] & 8) >> 1);
+          const int pp = (pre.pr[fm] & ~12) | ((pre.pr[fm] & 4) << 1) | ((pre.pr[fm] & 8) >> 1);
 #pragma unroll
           for (int pass = 0; pass < 4; ++pass) {
             const int cf = pass * 8 + (lane >> 3);
@@ -461,7 +598,7 @@ struct EpiQkv {
             const float2 cs = o.rope[p * kRopeFreqs + fi];
             const float x0 = acc[fm][fp][r] + b0, x1 = acc[fm][fp + 1][r] + b1;
             const float qs = region ? 1.0f : kQScaleLog2;
-            const uint16_t y0 = bf16_bits((x0 * cs.x - x1 * cs.y) * qs), y1 = bf16_bits((x1 * cs.x + x0 * cs.y) * qs);
+            const uint16_t y0 = bf16_bits(rot0(x0, x1, cs) * qs), y1 = bf16_bits(rot1(x0, x1, cs) * qs);
             if (region) {
               kdst[kc_offset(head, o.P, ti.y, j)] = y0;
               kdst[kc_offset(head, o.P, ti.y, j + kHeadDim / 2)] = y1;
@@ -651,9 +788,10 @@ static hipError_t launch_ws(const void* A, int lda, const void* B, int ldb, int 
 // 448x448 image's MLP up-projection: 8 x 32 tiles); 128x128 for other mid
 // sizes; 64x128 with the K split over two wave groups when N is narrow and M
 // small.  The 128x160 and 128x128 tilings run warp-specialized (producer
-// waves own the LDS-DMA), which measured 5-15% faster there.  The q/k/v
-// epilogue needs wave tiles whose width is a multiple of 64, which 32x160
-// is not.
+// waves own the LDS-DMA), which measured 5-15% faster there; four producers
+// of 8 loads a stage each for 128x128 (q/k/v at 448x448: 21.1 -> 20.2 us
+// against two of 16).  The q/k/v epilogue needs wave tiles whose width is a
+// multiple of 64, which 32x160 is not.
 template <int KT, bool ALLOW160, class Epi, class RowMap>
 static hipError_t run_pipe(const void* A, int lda, const void* B, int ldb, int M, int N, const Epi& epi,
                            RowMap rmap, hipStream_t s) {
@@ -688,7 +826,7 @@ static hipError_t run_pipe(const void* A, int lda, const void* B, int ldb, int M
   if constexpr (ALLOW160)
     if (N % 160 == 0 && t160 >= 192 && t160 <= 256)
       return launch_ws<128, 160, 4, 1, 4, KT, 4>(A, lda, B, ldb, M, N, epi, rmap, s);
-  if (t128 >= 200) return launch_ws<128, 128, 4, 2, 4, KT, 2>(A, lda, B, ldb, M, N, epi, rmap, s);
+  if (t128 >= 200) return launch_ws<128, 128, 4, 2, 4, KT, 4>(A, lda, B, ldb, M, N, epi, rmap, s);
   // few tiles: two wave groups split K inside each workgroup
   return launch_pipe<64, 128, 2, 2, 3, KT, 2>(A, lda, B, ldb, M, N, epi, rmap, s);
 }
@@ -908,11 +1046,34 @@ struct EpiColScale {
         for (int r = 0; r < 16; ++r) acc[fm][fn][r] *= sc;
     }
   }
+  // the column scales and the inner epilogue's values, before the K loop
+  template <int FM, int FN>
+  struct Pre {
+    typename Inner::template Pre<FM, FN> in;
+    float sc[FN];
+  };
+  template <int FM, int FN, bool DEEP>
+  __device__ __forceinline__ Pre<FM, FN> prefetch(int wm0, int wn0, int lane, int M, int N, bool active) const {
+    Pre<FM, FN> p;
+    if (!active) return p;
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      const int col = QV_ACC_COL(wn0, fn, lane);
+      p.sc[fn] = col < N ? scale[rm(col)] : 0.f;
+    }
+    p.in = in.template prefetch<FM, FN, DEEP>(wm0, wn0, lane, M, N, true);
+    return p;
+  }
   template <int FM, int FN>
   __device__ __forceinline__ void apply_staged(f32x16 (&acc)[FM][FN], float* wlds, int wm0, int wn0, int lane, int M,
-                                               int N) const {
-    scale_acc(acc, wn0, lane, N);
-    in.apply_staged(acc, wlds, wm0, wn0, lane, M, N);
+                                               int N, const Pre<FM, FN>& pre) const {
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[fm][fn][r] *= pre.sc[fn];
+    in.apply_staged(acc, wlds, wm0, wn0, lane, M, N, pre.in);
   }
   template <int FM, int FN>
   __device__ __forceinline__ void apply(f32x16 (&acc)[FM][FN], int wm0, int wn0, int lane, int M, int N) const {

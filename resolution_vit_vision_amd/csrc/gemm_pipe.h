@@ -259,6 +259,10 @@ __global__ __launch_bounds__(WM * WN * KS * 64) void k_gemm_pipe(const uint16_t*
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // epilogue values (issued before the ring, so waiting for them never
+  // waits for a ring load)
+  const auto pre = epi.template prefetch<C::FM, C::FN, false>(m0 + wm * C::TM, n0 + wn * C::TN, lane, M, N, kgrp == 0);
+
   // prologue: STAGES - 1 steps in flight
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
@@ -296,7 +300,7 @@ __global__ __launch_bounds__(WM * WN * KS * 64) void k_gemm_pipe(const uint16_t*
         for (int r = 0; r < 16; ++r) acc[i][j][r] += slot[((i * C::FN + j) * 16 + r) * 64 + lane];
   }
   if constexpr (Epi::kStaged) {
-    epi.apply_staged(acc, slot, m0 + wm * C::TM, n0 + wn * C::TN, lane, M, N);
+    epi.apply_staged(acc, slot, m0 + wm * C::TM, n0 + wn * C::TN, lane, M, N, pre);
   } else {
     epi.apply(acc, m0 + wm * C::TM, n0 + wn * C::TN, lane, M, N);
   }
@@ -428,6 +432,9 @@ __global__ __launch_bounds__((WM * WN + NP) * 64) void k_gemm_ws(const uint16_t*
   }
 
   const int wm = wave / WN, wn = wave % WN;
+  // epilogue values: a consumer issues no ring loads, so its dependent loads
+  // (rotary entries after token info) cost the K loop nothing
+  const auto pre = epi.template prefetch<C::FM, C::FN, true>(m0 + wm * C::TM, n0 + wn * C::TN, lane, M, N, true);
   f32x16 acc[C::FM][C::FN];
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
@@ -446,7 +453,7 @@ __global__ __launch_bounds__((WM * WN + NP) * 64) void k_gemm_ws(const uint16_t*
   uint16_t* sbuf = sb == 0 ? st0 : sb == 1 ? st1 : sb == 2 ? st2 : sb == 3 ? st3 : sb == 4 ? st4 : sb == 5 ? st5
                  : sb == 6 ? st6 : st7;
   float* slot = reinterpret_cast<float*>(sbuf) + (wave % PER) * SLOT;
-  epi.apply_staged(acc, slot, m0 + wm * C::TM, n0 + wn * C::TN, lane, M, N);
+  epi.apply_staged(acc, slot, m0 + wm * C::TM, n0 + wn * C::TN, lane, M, N, pre);
 }
 
 // ------------------------------------------- int8 weights (warp-specialized)
@@ -621,6 +628,7 @@ __global__ __launch_bounds__((WM * WN + NPA + NPB) * 64) void k_gemm_ws_i8(
   }
 
   const int wm = wave / WN, wn = wave % WN;
+  const auto pre = epi.template prefetch<C::FM, C::FN, true>(m0 + wm * C::TM, n0 + wn * C::TN, lane, M, N, true);
   // this lane's output columns' weight-row scales, fetched before the loop
   float sc[C::FN];
 #pragma unroll
@@ -650,7 +658,7 @@ __global__ __launch_bounds__((WM * WN + NPA + NPB) * 64) void k_gemm_ws_i8(
   const int sb = wave / PER;
   uint16_t* sbuf = sb == 0 ? st0 : sb == 1 ? st1 : sb == 2 ? st2 : st3;
   float* slot = reinterpret_cast<float*>(sbuf) + (wave % PER) * SLOT;
-  epi.apply_staged(acc, slot, m0 + wm * C::TM, n0 + wn * C::TN, lane, M, N);
+  epi.apply_staged(acc, slot, m0 + wm * C::TM, n0 + wn * C::TN, lane, M, N, pre);
 }
 
 }  // namespace qv
