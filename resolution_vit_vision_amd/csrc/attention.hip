@@ -420,7 +420,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
     int blk = wave + NW * i;
     blk = blk < BLKS ? blk : BLKS - 1;
     const int slot = blk * 64 + lane;
-    if (slot < K_BYTES / 16) {
+    if (blk < K_BYTES / 1024) {  // whole blocks: the same for every lane
       goff[i] = (uint32_t)slot * 16;
       isk[i] = true;
     } else {
@@ -624,6 +624,71 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
     }                                                                                                        \
     s_cur = s_nxt;                                                                                           \
   }
+  // Steady step: the fast pass's step for a tile whose successor is a whole
+  // tile and whose loads three tiles ahead exist (no mask, no bounds tests),
+  // so the step's VALU work is its 16 exponentials and 8 packs alone and the
+  // step after the barrier is one basic block for the scheduler (the general
+  // step's mask test split it in two and cost two VALU instructions a step).
+  // 65,536-patch block 18.30 -> 17.83 ms, 4 x 672x672 and the mixed batch
+  // -2.5 %, output bit for bit the same.
+#define QV_L_STEADY(IT, ST)                                                                                  \
+  {                                                                                                          \
+    if (nblk == LWMAX) QV_WAIT_VM(LWMAX); else QV_WAIT_VM(LWMAX - 1);                                        \
+    QV_BARRIER();                                                                                            \
+    QV_L_ISSUE((IT) + 3, ((ST) + 3) % NST)                                                                   \
+    bf16x8 kf_[5];                                                                                           \
+    _Pragma("unroll") for (int kk = 0; kk < 5; ++kk)                                                        \
+      kf_[kk] = *reinterpret_cast<const bf16x8*>(lds + (((ST) + 1) % NST) * STRIDE + kk * 1024 + koff);     \
+    s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf_[0], qf[0], negm, 0, 0, 0);                          \
+    _Pragma("unroll") for (int kk = 1; kk < 5; ++kk)                                                        \
+      s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf_[kk], qf[kk], s_nxt, 0, 0, 0);                      \
+    bf16x8 pb[2];                                                                                            \
+    _Pragma("unroll") for (int e = 0; e < 8; ++e)                                                            \
+      pb[0][e] = (__bf16)__builtin_amdgcn_exp2f(s_cur[e]);                                                   \
+    bf16x8 vf_[6];                                                                                           \
+    _Pragma("unroll") for (int s2 = 0; s2 < 2; ++s2)                                                         \
+    _Pragma("unroll") for (int t = 0; t < 3; ++t)                                                            \
+      vf_[3 * s2 + t] = *reinterpret_cast<const bf16x8*>(lds + (ST) * STRIDE +                               \
+                                                       (t < 2 ? voff[s2] + t * 2048 : voff2[s2]));           \
+    asm volatile("" ::"v"(pb[0]));                                                                           \
+    __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);                                                       \
+    __builtin_amdgcn_sched_group_barrier(0x402, 2, 0);                                                       \
+    _Pragma("unroll") for (int g_ = 0; g_ < 5; ++g_) {                                                       \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                     \
+      __builtin_amdgcn_sched_group_barrier(0x402, 2, 0);                                                     \
+    }                                                                                                        \
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);                                                       \
+    _Pragma("unroll") for (int t = 0; t < 3; ++t)                                                            \
+      o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf_[t], pb[0], o[t], 0, 0, 0);                          \
+    _Pragma("unroll") for (int e = 0; e < 8; ++e)                                                            \
+      pb[1][e] = (__bf16)__builtin_amdgcn_exp2f(s_cur[8 + e]);                                               \
+    _Pragma("unroll") for (int t = 0; t < 3; ++t)                                                            \
+      o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf_[3 + t], pb[1], o[t], 0, 0, 0);                      \
+    _Pragma("unroll") for (int g_ = 0; g_ < 6; ++g_) {                                                       \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                     \
+      __builtin_amdgcn_sched_group_barrier(0x402, 2, 0);                                                     \
+    }                                                                                                        \
+    s_cur = s_nxt;                                                                                           \
+  }
+#define QV_L_LOOP_FAST()                                                                                     \
+  {                                                                                                          \
+    int it = 0;                                                                                              \
+    for (; it + 7 <= iters; it += NST) {                                                                     \
+      QV_L_STEADY(it, 0)                                                                                     \
+      QV_L_STEADY(it + 1, 1)                                                                                 \
+      QV_L_STEADY(it + 2, 2)                                                                                 \
+      QV_L_STEADY(it + 3, 3)                                                                                 \
+    }                                                                                                        \
+    for (; it < iters; it += NST) {                                                                          \
+      QV_L_STEP(it, 0, false)                                                                                \
+      if (it + 1 >= iters) break;                                                                            \
+      QV_L_STEP(it + 1, 1, false)                                                                            \
+      if (it + 2 >= iters) break;                                                                            \
+      QV_L_STEP(it + 2, 2, false)                                                                            \
+      if (it + 3 >= iters) break;                                                                            \
+      QV_L_STEP(it + 3, 3, false)                                                                            \
+    }                                                                                                        \
+  }
 #define QV_L_LOOP(LAZY)                                                                                      \
   for (int it = 0; it < iters; it += NST) {                                                                  \
     QV_L_STEP(it, 0, LAZY)                                                                                   \
@@ -643,7 +708,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
   // maximum, which bounds every exponent.
   QV_L_PROLOGUE()
   QV_L_FIRST()
-  QV_L_LOOP(false)
+  QV_L_LOOP_FAST()
   {
     float chk = 0.f;
 #pragma unroll
@@ -664,6 +729,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
     }
   }
 #undef QV_L_LOOP
+#undef QV_L_LOOP_FAST
+#undef QV_L_STEADY
 #undef QV_L_STEP
 #undef QV_L_FIRST
 #undef QV_L_PROLOGUE
