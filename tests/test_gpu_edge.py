@@ -168,3 +168,42 @@ def test_long_attention_overflow_redoes_with_running_max():
     e = rel_l2(got - z, ref - z)
     _say(f"  block update rel-L2 {e:.3e}")
     assert e <= 2e-2
+
+
+def test_long_attention_key_loop_tails():
+    """The long-sequence attention kernel runs its key loop in whole-tile
+    steady steps while the next tile is whole and three tiles ahead exist,
+    then finishes with the general step (mask on the last tile).  Seven packed
+    images of 2080-2200 patches (enough 128-row query tiles to take that
+    kernel) give every remainder of the key-tile count modulo the unroll of
+    4 and last tiles of 4, 16, 20 and 24 keys as well as whole ones; each image's
+    loop ends on its own tail.  The block's update (output minus input) must
+    match the oracle's."""
+    qv = _qv()
+    shapes = [(46, 46), (42, 50), (40, 52), (16, 134), (48, 44), (44, 50), (40, 54)]   # patches per side
+    images = [(14 * a, 14 * b, 1) for a, b in shapes]
+    ns = [a * b for a, b in shapes]
+    tiles = [(n + 31) // 32 for n in ns]
+    assert {t % 4 for t in tiles} == {0, 1, 2, 3}
+    assert {n % 32 for n in ns} >= {0, 4, 16, 20, 24}
+    wl = synth.small_workload("tails", images, depth=1)
+    params, imgs = synth.params(wl), synth.pixels(wl)
+    grids = [O.grid_thw(h, w, f)[2] for h, w, f in images]
+    _say(f"long attention tails: n={ns} key tiles={tiles}")
+    enc0 = qv.Encoder(params, imgs, depth=0, out_dim=1536)
+    enc0.run()
+    enc1 = qv.Encoder(params, imgs, depth=1, out_dim=1536)
+    enc1.run()
+    torch.cuda.synchronize()
+    assert enc1.grids == [tuple(g) for g in grids]
+    x = O.patchify(imgs, grids)
+    z0 = O.vision_forward(x, params, grids, 0)
+    z1 = O.vision_forward(x, params, grids, 1)
+    g0 = enc0.hidden.float().cpu().numpy().astype(np.float64)
+    g1 = enc1.hidden.float().cpu().numpy().astype(np.float64)
+    cu = np.concatenate([[0], np.cumsum(ns)])
+    for i in range(len(ns)):
+        a, b = cu[i], cu[i + 1]
+        e = rel_l2(g1[a:b] - g0[a:b], z1[a:b] - z0[a:b])
+        _say(f"  image {i}: n={ns[i]} tiles={tiles[i]} block update rel-L2 {e:.3e}")
+        assert e <= 2e-2
