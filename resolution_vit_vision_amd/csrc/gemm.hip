@@ -791,9 +791,9 @@ static hipError_t launch_ws(const void* A, int lda, const void* B, int ldb, int 
 // 448x448 image's MLP up-projection: 8 x 32 tiles); 128x128 for other mid
 // sizes; 64x128 with the K split over two wave groups when N is narrow and M
 // small.  The 128x160 and 128x128 tilings run warp-specialized (producer
-// waves own the LDS-DMA), which measured 5-15% faster there; four producers
-// of 8 loads a stage each for 128x128 (q/k/v at 448x448: 21.1 -> 20.2 us
-// against two of 16).  The q/k/v epilogue needs wave tiles whose width is a
+// waves own the LDS-DMA), which measured 5-15% faster there; eight producers
+// of 4 loads a stage each for 128x128 (q/k/v at 448x448: 21.1 us with two
+// producers, 20.2 with four, 18.7 with eight).  The q/k/v epilogue needs wave tiles whose width is a
 // multiple of 64, which 32x160 is not.
 template <int KT, bool ALLOW160, class Epi, class RowMap>
 static hipError_t run_pipe(const void* A, int lda, const void* B, int ldb, int M, int N, const Epi& epi,
@@ -829,7 +829,7 @@ static hipError_t run_pipe(const void* A, int lda, const void* B, int ldb, int M
   if constexpr (ALLOW160)
     if (N % 160 == 0 && t160 >= 192 && t160 <= 256)
       return launch_ws<128, 160, 4, 1, 4, KT, 4>(A, lda, B, ldb, M, N, epi, rmap, s);
-  if (t128 >= 200) return launch_ws<128, 128, 4, 2, 4, KT, 4>(A, lda, B, ldb, M, N, epi, rmap, s);
+  if (t128 >= 200) return launch_ws<128, 128, 4, 2, 4, KT, 8>(A, lda, B, ldb, M, N, epi, rmap, s);
   // few tiles: two wave groups split K inside each workgroup
   return launch_pipe<64, 128, 2, 2, 3, KT, 2>(A, lda, B, ldb, M, N, epi, rmap, s);
 }
@@ -883,9 +883,12 @@ hipError_t gemm_bf16_splitk_f32(const void* A, int lda, const void* B, int ldb, 
   if (M <= 0 || N <= 0) return hipSuccess;
   if (splits < 1 || N % 160 || K % 64 || (K / 64) % splits || lda % 8 || ldb % 8) return hipErrorInvalidValue;
   const EpiPartF32 e{P, N, (size_t)M * N};
+  // six producer waves (fc2 at 448x448: 21.5 -> 21.1 us against four); the
+  // activation epilogues of the same tile keep four, which leaves their
+  // consumers the registers they need without spilling
   switch (K / 64 / splits) {
-    case 20: return launch_ws<128, 160, 4, 1, 4, 20, 4>(A, lda, B, ldb, M, N, e, RowMapIdentity{}, s, splits);
-    case 40: return launch_ws<128, 160, 4, 1, 4, 40, 4>(A, lda, B, ldb, M, N, e, RowMapIdentity{}, s, splits);
+    case 20: return launch_ws<128, 160, 4, 1, 4, 20, 6>(A, lda, B, ldb, M, N, e, RowMapIdentity{}, s, splits);
+    case 40: return launch_ws<128, 160, 4, 1, 4, 40, 6>(A, lda, B, ldb, M, N, e, RowMapIdentity{}, s, splits);
     default: return hipErrorInvalidValue;
   }
 }
