@@ -761,13 +761,13 @@ static XcdCut xcd_cut(int tiles_m, int tiles_n, int BM, int BN) {
   return best;
 }
 
-template <int BM, int BN, int WM, int WN, int ST, int KT, int KS = 1, class Epi, class RowMap>
+template <int BM, int BN, int WM, int WN, int ST, int KT, class Epi, class RowMap>
 static hipError_t launch_pipe(const void* A, int lda, const void* B, int ldb, int M, int N, const Epi& epi,
                               RowMap rmap, hipStream_t s) {
   // the kernel addresses its operands with 32-bit byte offsets below 2 GiB
   if ((size_t)M * lda * 2 >= 0x7FFFFFFFu || (size_t)N * ldb * 2 >= 0x7FFFFFFFu) return hipErrorInvalidValue;
   const XcdCut cut = xcd_cut((M + BM - 1) / BM, (N + BN - 1) / BN, BM, BN);
-  QV_KLAUNCH((k_gemm_pipe<BM, BN, WM, WN, ST, KT / KS, KS, Epi, RowMap>), dim3(cut.grid), dim3(WM * WN * KS * 64),
+  QV_KLAUNCH((k_gemm_pipe<BM, BN, WM, WN, ST, KT, Epi, RowMap>), dim3(cut.grid), dim3(WM * WN * 64),
                      0, s, reinterpret_cast<const uint16_t*>(A), lda, reinterpret_cast<const uint16_t*>(B), ldb, M, N,
                      cut.xgn, 8, epi, rmap);
   return hipGetLastError();
@@ -789,12 +789,15 @@ static hipError_t launch_ws(const void* A, int lda, const void* B, int ldb, int 
 // direct pipeline) when that already fills the GPU; 128x160 when N is a
 // multiple of 160 and that tiling fills one wave of 256 workgroups (the
 // 448x448 image's MLP up-projection: 8 x 32 tiles); 128x128 for other mid
-// sizes; 64x128 with the K split over two wave groups when N is narrow and M
-// small.  The 128x160 and 128x128 tilings run warp-specialized (producer
-// waves own the LDS-DMA), which measured 5-15% faster there; eight producers
-// of 4 loads a stage each for 128x128 (q/k/v at 448x448: 21.1 us with two
-// producers, 20.2 with four, 18.7 with eight).  The q/k/v epilogue needs wave tiles whose width is a
-// multiple of 64, which 32x160 is not.
+// sizes; 64x128 when N is narrow and M small.  The 128x160, 128x128 and
+// 64x128 tilings run warp-specialized (producer waves own the LDS-DMA),
+// which measured 5-15% faster there; eight producers of 4 loads a stage
+// each for 128x128 (q/k/v at 448x448: 21.1 us with two producers, 20.2 with
+// four, 18.7 with eight), eight of 3 for 64x128 (the out-projection at
+// 448x448: 14.2 us with the K range split over two groups of four waves
+// that all load, 13.5 with four consumers and eight producers).  The q/k/v
+// epilogue needs wave tiles whose width is a multiple of 64, which 32x160
+// is not.
 template <int KT, bool ALLOW160, class Epi, class RowMap>
 static hipError_t run_pipe(const void* A, int lda, const void* B, int ldb, int M, int N, const Epi& epi,
                            RowMap rmap, hipStream_t s) {
@@ -830,8 +833,8 @@ static hipError_t run_pipe(const void* A, int lda, const void* B, int ldb, int M
     if (N % 160 == 0 && t160 >= 192 && t160 <= 256)
       return launch_ws<128, 160, 4, 1, 4, KT, 4>(A, lda, B, ldb, M, N, epi, rmap, s);
   if (t128 >= 200) return launch_ws<128, 128, 4, 2, 4, KT, 8>(A, lda, B, ldb, M, N, epi, rmap, s);
-  // few tiles: two wave groups split K inside each workgroup
-  return launch_pipe<64, 128, 2, 2, 3, KT, 2>(A, lda, B, ldb, M, N, epi, rmap, s);
+  // few tiles: 64x128, four consumers of 32x64, eight producers
+  return launch_ws<64, 128, 2, 2, 4, KT, 8>(A, lda, B, ldb, M, N, epi, rmap, s);
 }
 
 template <class Epi, class RowMap>

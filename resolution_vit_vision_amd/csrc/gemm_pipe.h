@@ -41,29 +41,22 @@ typedef __attribute__((address_space(3))) void* las_ptr;
 
 __device__ __forceinline__ int swz_chunk(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
-// KS wave groups of WM x WN waves share one LDS ring; every pipeline step
-// stages KS consecutive 64-deep k-tiles and group g multiplies the g-th one,
-// so each group walks half of K when KS = 2 (the partial sums are added
-// through LDS at the end).  This doubles the waves per workgroup (and halves
-// the serial K loop) when the output alone gives too few workgroups.
-template <int BM_, int BN_, int WM, int WN, int STAGES, int KS_ = 1>
+// WM x WN waves share one LDS ring of STAGES 64-deep k-tiles of A and B.
+template <int BM_, int BN_, int WM, int WN, int STAGES>
 struct PipeCfg {
-  static constexpr int BM = BM_, BN = BN_, KS = KS_;
-  static constexpr int NWG = WM * WN;                         // waves per group
-  static constexpr int NW = NWG * KS_;
+  static constexpr int BM = BM_, BN = BN_;
+  static constexpr int NW = WM * WN;
   static constexpr int NT = NW * 64;
   static constexpr int BK = 64;
   static constexpr int TM = BM_ / WM, TN = BN_ / WN;
   static constexpr int FM = TM / 32, FN = TN / 32;
-  static constexpr int SUB_ELEMS = (BM_ + BN_) * BK;          // one 64-deep k-tile of A and B
-  static constexpr int STAGE_ELEMS = SUB_ELEMS * KS_;         // bf16 elements per stage
-  static constexpr int LOADS_A = BM_ * 8 * KS_ / NT;          // 16-byte chunks per thread per stage
-  static constexpr int LOADS_B = BN_ * 8 * KS_ / NT;
+  static constexpr int STAGE_ELEMS = (BM_ + BN_) * BK;        // bf16 elements per stage (A, then B)
+  static constexpr int LOADS_A = BM_ * 8 / NT;                // 16-byte chunks per thread per stage
+  static constexpr int LOADS_B = BN_ * 8 / NT;
   static constexpr int LOADS = LOADS_A + LOADS_B;             // vmcnt of one stage per wave
   static_assert(FM >= 1 && FN >= 1, "wave tile at least 32x32");
-  static_assert(BM_ * 8 % (NWG * 64) == 0 && BN_ * 8 % (NWG * 64) == 0, "whole 1 KB chunks per wave");
+  static_assert(BM_ * 8 % NT == 0 && BN_ * 8 % NT == 0, "whole 1 KB chunks per wave");
   static_assert(STAGES >= 2 && STAGES <= 8, "2..8 stages");
-  static_assert(KS_ == 1 || KS_ == 2, "K split 1 or 2");
 };
 
 // The loads are buffer_load ... lds (MUBUF) rather than global_load_lds:
@@ -87,30 +80,28 @@ __device__ __forceinline__ void pipe_setup(PipeState<C>& ps, const uint16_t* A, 
                                            int M, int N, int m0, int n0, RowMap rmap, int wave, int lane) {
 #pragma unroll
   for (int i = 0; i < C::LOADS; ++i) {
-    // 1 KB block index inside the stage: per k sub-tile, A blocks first, then B blocks
+    // 1 KB block index inside the stage: A blocks first, then B blocks
     const int blk = i * C::NW + wave;
     const int p = blk * 64 + lane;              // 16-byte slot inside the stage
-    const int ks = p / ((C::BM + C::BN) * 8);   // k sub-tile
-    const int pq = p % ((C::BM + C::BN) * 8);
-    const bool isA = pq < C::BM * 8;
-    const int q = isA ? pq : pq - C::BM * 8;
+    const bool isA = p < C::BM * 8;
+    const int q = isA ? p : p - C::BM * 8;
     const int r = q >> 3;                       // tile row
     const int c = swz_chunk(r, q & 7);          // logical k chunk stored at this slot
     if (isA) {
       int g = m0 + r;
       g = g < M ? g : M - 1;
-      ps.voff[i] = (uint32_t)(((size_t)g * lda + ks * 64 + c * 8) * 2);
+      ps.voff[i] = (uint32_t)(((size_t)g * lda + c * 8) * 2);
     } else {
       int g = n0 + r;
       g = g < N ? g : N - 1;
-      ps.voff[i] = (uint32_t)(((size_t)rmap(g) * ldb + ks * 64 + c * 8) * 2);
+      ps.voff[i] = (uint32_t)(((size_t)rmap(g) * ldb + c * 8) * 2);
     }
     ps.ldst[i] = (uint32_t)(blk * 1024);
   }
   uint32_t am = 0;
 #pragma unroll
   for (int i = 0; i < C::LOADS; ++i)
-    if ((((i * C::NW + wave) * 64) % ((C::BM + C::BN) * 8)) < C::BM * 8) am |= 1u << i;
+    if ((i * C::NW + wave) * 64 < C::BM * 8) am |= 1u << i;
   ps.amask = am;
   ps.abase = A;
   ps.bbase = B;
@@ -126,9 +117,9 @@ __device__ __forceinline__ void pipe_issue(const PipeState<C>& ps, uint16_t* sta
   for (int i = 0; i < C::LOADS; ++i) {
     char* dst = reinterpret_cast<char*>(stage) + ps.ldst[i];
     if ((ps.amask >> i) & 1u)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (las_ptr)dst, 16, ps.voff[i], kt * 128 * C::KS, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (las_ptr)dst, 16, ps.voff[i], kt * 128, 0, 0);
     else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (las_ptr)dst, 16, ps.voff[i], kt * 128 * C::KS, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (las_ptr)dst, 16, ps.voff[i], kt * 128, 0, 0);
   }
 #endif
 }
@@ -209,25 +200,25 @@ template <class C, int KT, int STAGES>
 struct PipeSteps {
   template <int kt>
   static __device__ __forceinline__ void run(uint16_t* const (&st)[8], const PipeState<C>& ps,
-                                             f32x16 (&acc)[C::FM][C::FN], int wm, int wn, int lane, int sub) {
+                                             f32x16 (&acc)[C::FM][C::FN], int wm, int wn, int lane) {
     if constexpr (kt < KT) {
       constexpr int later = (KT - 1 - kt) < (STAGES - 2) ? (KT - 1 - kt) : (STAGES - 2);
       QV_WAIT_VM(later * C::LOADS);
       QV_BARRIER();
       if constexpr (kt + STAGES - 1 < KT) pipe_issue<C>(ps, st[(kt + STAGES - 1) % STAGES], kt + STAGES - 1);
-      pipe_compute<C>(st[kt % STAGES] + sub, acc, wm, wn, lane);
-      run<kt + 1>(st, ps, acc, wm, wn, lane, sub);
+      pipe_compute<C>(st[kt % STAGES], acc, wm, wn, lane);
+      run<kt + 1>(st, ps, acc, wm, wn, lane);
     }
   }
 };
 
-// KT = (K / 64) / KS pipeline steps is a compile-time constant (the tower's K
-// is 1280 or 5120).
-template <int BM, int BN, int WM, int WN, int STAGES, int KT, int KS, class Epi, class RowMap>
-__global__ __launch_bounds__(WM * WN * KS * 64) void k_gemm_pipe(const uint16_t* __restrict__ A, int lda,
-                                                                 const uint16_t* __restrict__ B, int ldb, int M,
-                                                                 int N, int xgn, int group, Epi epi, RowMap rmap) {
-  using C = PipeCfg<BM, BN, WM, WN, STAGES, KS>;
+// KT = K / 64 pipeline steps is a compile-time constant (the tower's K is
+// 1280 or 5120).
+template <int BM, int BN, int WM, int WN, int STAGES, int KT, class Epi, class RowMap>
+__global__ __launch_bounds__(WM * WN * 64) void k_gemm_pipe(const uint16_t* __restrict__ A, int lda,
+                                                            const uint16_t* __restrict__ B, int ldb, int M, int N,
+                                                            int xgn, int group, Epi epi, RowMap rmap) {
+  using C = PipeCfg<BM, BN, WM, WN, STAGES>;
   constexpr int SE = C::STAGE_ELEMS;
   __shared__ __attribute__((aligned(1024))) uint16_t st0[SE];
   __shared__ __attribute__((aligned(1024))) uint16_t st1[SE];
@@ -241,8 +232,7 @@ __global__ __launch_bounds__(WM * WN * KS * 64) void k_gemm_pipe(const uint16_t*
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kgrp = wave / C::NWG, wig = wave % C::NWG;  // k group, wave inside the group
-  const int wm = wig / WN, wn = wig % WN;
+  const int wm = wave / WN, wn = wave % WN;
   const int tiles_n = (N + BN - 1) / BN, tiles_m = (M + BM - 1) / BM;
   int tm, tn;
   if (!tile_coords(blockIdx.x, tiles_m, tiles_n, xgn, group, tm, tn)) return;  // uniform over the workgroup
@@ -261,44 +251,24 @@ __global__ __launch_bounds__(WM * WN * KS * 64) void k_gemm_pipe(const uint16_t*
 
   // epilogue values (issued before the ring, so waiting for them never
   // waits for a ring load)
-  const auto pre = epi.template prefetch<C::FM, C::FN, false>(m0 + wm * C::TM, n0 + wn * C::TN, lane, M, N, kgrp == 0);
+  const auto pre = epi.template prefetch<C::FM, C::FN, false>(m0 + wm * C::TM, n0 + wn * C::TN, lane, M, N, true);
 
   // prologue: STAGES - 1 steps in flight
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
     if (s < KT) pipe_issue<C>(ps, st[s], s);
-  PipeSteps<C, KT, STAGES>::template run<0>(st, ps, acc, wm, wn, lane, kgrp * C::SUB_ELEMS);
+  PipeSteps<C, KT, STAGES>::template run<0>(st, ps, acc, wm, wn, lane);
 
-  constexpr int ACC_FLOATS = KS == 2 ? C::FM * C::FN * 16 * 64 : 0;  // one wave's accumulators
-  constexpr int SLOT = ACC_FLOATS > Epi::kPatchFloats ? ACC_FLOATS : Epi::kPatchFloats;
-  // every wave is done reading the ring: reuse stage 0 (and 1) as one slot per
-  // wave of the first group, for the k-group reduction and then the staged
-  // epilogue patch of that wave
+  constexpr int SLOT = Epi::kPatchFloats;
+  // every wave is done reading the ring: reuse it as one staged-epilogue
+  // patch per wave
   constexpr int PER = (SE * 2) / (SLOT * 4);
-  static_assert(PER >= 1 && PER * STAGES >= C::NWG, "per-wave slots fit in the ring");
+  static_assert(PER >= 1 && PER * STAGES >= C::NW, "per-wave slots fit in the ring");
   QV_BARRIER();
-  const int sb = wig / PER;
+  const int sb = wave / PER;
   uint16_t* sbuf = sb == 0 ? st0 : sb == 1 ? st1 : sb == 2 ? st2 : sb == 3 ? st3 : sb == 4 ? st4 : sb == 5 ? st5
                  : sb == 6 ? st6 : st7;
-  float* slot = reinterpret_cast<float*>(sbuf) + (wig % PER) * SLOT;
-  if constexpr (KS == 2) {
-    if (kgrp == 1) {
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) slot[((i * C::FN + j) * 16 + r) * 64 + lane] = acc[i][j][r];
-    }
-    QV_BARRIER();
-    if (kgrp == 1) return;
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] += slot[((i * C::FN + j) * 16 + r) * 64 + lane];
-  }
+  float* slot = reinterpret_cast<float*>(sbuf) + (wave % PER) * SLOT;
   if constexpr (Epi::kStaged) {
     epi.apply_staged(acc, slot, m0 + wm * C::TM, n0 + wn * C::TN, lane, M, N, pre);
   } else {
@@ -392,7 +362,7 @@ template <int BM, int BN, int WM, int WN, int STAGES, int KT, int NP, class Epi,
 __global__ __launch_bounds__((WM * WN + NP) * 64) void k_gemm_ws(const uint16_t* __restrict__ A, int lda,
                                                                 const uint16_t* __restrict__ B, int ldb, int M,
                                                                 int N, int xgn, int group, Epi epi_all, RowMap rmap) {
-  using C = PipeCfg<BM, BN, WM, WN, STAGES, 1>;
+  using C = PipeCfg<BM, BN, WM, WN, STAGES>;
   constexpr int NC = WM * WN;
   constexpr int BLOCKS = (BM + BN) * 8 / 64;  // 1 KB blocks per stage
   constexpr int LP = BLOCKS / NP;
@@ -584,7 +554,7 @@ template <int BM, int BN, int WM, int WN, int STAGES, int KT, int NPA, int NPB, 
 __global__ __launch_bounds__((WM * WN + NPA + NPB) * 64) void k_gemm_ws_i8(
     const uint16_t* __restrict__ A, int lda, const int8_t* __restrict__ B, int ldb, const float* __restrict__ bscale,
     int M, int N, int xgn, int group, Epi epi_all, RowMap rmap) {
-  using C = PipeCfg<BM, BN, WM, WN, STAGES, 1>;
+  using C = PipeCfg<BM, BN, WM, WN, STAGES>;
   constexpr int NC = WM * WN;
   constexpr int ABLK = BM * 8 / 64;
   constexpr int LPA = ABLK / NPA;
