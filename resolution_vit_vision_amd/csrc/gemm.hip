@@ -903,9 +903,9 @@ hipError_t gemm_bf16_splitk_any_f32(const void* A, int lda, const void* B, int l
   if (splits < 1 || N % 128 || K % 64 || (K / 64) % splits || lda % 8 || ldb % 8) return hipErrorInvalidValue;
   const EpiPartF32 e{P, N, (size_t)M * N};
   switch (K / 64 / splits) {
-    case 10: return launch_ws<128, 128, 4, 2, 4, 10, 2>(A, lda, B, ldb, M, N, e, RowMapIdentity{}, s, splits);
-    case 20: return launch_ws<128, 128, 4, 2, 4, 20, 2>(A, lda, B, ldb, M, N, e, RowMapIdentity{}, s, splits);
-    case 40: return launch_ws<128, 128, 4, 2, 4, 40, 2>(A, lda, B, ldb, M, N, e, RowMapIdentity{}, s, splits);
+    case 10: return launch_ws<128, 128, 4, 2, 4, 10, 8>(A, lda, B, ldb, M, N, e, RowMapIdentity{}, s, splits);
+    case 20: return launch_ws<128, 128, 4, 2, 4, 20, 8>(A, lda, B, ldb, M, N, e, RowMapIdentity{}, s, splits);
+    case 40: return launch_ws<128, 128, 4, 2, 4, 40, 8>(A, lda, B, ldb, M, N, e, RowMapIdentity{}, s, splits);
     default: return hipErrorInvalidValue;
   }
 }

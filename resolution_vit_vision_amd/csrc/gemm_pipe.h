@@ -55,7 +55,6 @@ struct PipeCfg {
   static constexpr int LOADS_B = BN_ * 8 / NT;
   static constexpr int LOADS = LOADS_A + LOADS_B;             // vmcnt of one stage per wave
   static_assert(FM >= 1 && FN >= 1, "wave tile at least 32x32");
-  static_assert(BM_ * 8 % NT == 0 && BN_ * 8 % NT == 0, "whole 1 KB chunks per wave");
   static_assert(STAGES >= 2 && STAGES <= 8, "2..8 stages");
 };
 
@@ -78,6 +77,7 @@ struct PipeState {
 template <class C, class RowMap>
 __device__ __forceinline__ void pipe_setup(PipeState<C>& ps, const uint16_t* A, int lda, const uint16_t* B, int ldb,
                                            int M, int N, int m0, int n0, RowMap rmap, int wave, int lane) {
+  static_assert(C::BM * 8 % C::NT == 0 && C::BN * 8 % C::NT == 0, "whole 1 KB chunks per wave");
 #pragma unroll
   for (int i = 0; i < C::LOADS; ++i) {
     // 1 KB block index inside the stage: A blocks first, then B blocks
