@@ -300,7 +300,7 @@ qv_status qv_vision_forward(const qv_vision_cfg *c, const qv_vision_w *w, const 
  * library, one copy on every GPU the library runs on, held until the process
  * ends.  A call whose qv_vision_workspace_size exceeds it returns
  * QV_ERR_WORKSPACE before anything is enqueued (a 448x448 image needs
- * 42.5 MiB, a 672x672 image 50.7 MiB; four packed 672x672 images do not
+ * 32.5 MiB, a 672x672 image 50.7 MiB; four packed 672x672 images do not
  * fit).  The array of the device current at the call is used, so `stream`
  * must belong to that device; its address is looked up on the first call on
  * each device.  Every call on one GPU shares that GPU's array and leaves its

@@ -243,6 +243,36 @@ __device__ __forceinline__ EpiPartF32 epi_at_split(const EpiPartF32& e, int s) {
   return r;
 }
 
+// The same partial sums rounded once to bf16 (the tower's split-K products,
+// whose runs launch_layernorm_acc adds): half the bytes written here and
+// read back there.  Each run's sum is rounded as a bf16 Linear rounds its
+// output; the runs, the bias and the residual are then added in float32.
+struct EpiPartBf16 {
+  static constexpr bool kStaged = true;
+  static constexpr int kPatchFloats = 32 * 40;
+  using RowParam = NoRowParam;
+  static constexpr int kRowParamFloats = 0;
+  uint16_t* C; int ldc; size_t stride;
+  __device__ float col_param(int) const { return 0.f; }
+  __device__ float pre(float, float v) const { return v; }
+  __device__ RowParam row_param(int, int) const { return {}; }
+  __device__ void store(int row, int col, const float (&v)[8], const RowParam&) const {
+    uint4 pk;
+    pk.x = pack_bf16(v[0], v[1]);
+    pk.y = pack_bf16(v[2], v[3]);
+    pk.z = pack_bf16(v[4], v[5]);
+    pk.w = pack_bf16(v[6], v[7]);
+    *reinterpret_cast<uint4*>(C + (size_t)row * ldc + col) = pk;
+  }
+  QV_STAGED_EPILOGUE(EpiPartBf16, 8)
+};
+
+__device__ __forceinline__ EpiPartBf16 epi_at_split(const EpiPartBf16& e, int s) {
+  EpiPartBf16 r = e;
+  r.C += (size_t)s * e.stride;
+  return r;
+}
+
 struct EpiResidF32 {
   static constexpr bool kStaged = true;
   static constexpr int kPatchFloats = 32 * 40;
@@ -896,6 +926,18 @@ hipError_t gemm_bf16_splitk_f32(const void* A, int lda, const void* B, int ldb, 
   }
 }
 
+hipError_t gemm_bf16_splitk_bf16(const void* A, int lda, const void* B, int ldb, int M, int N, int K, int splits,
+                                 uint16_t* P, hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (splits < 1 || N % 160 || K % 64 || (K / 64) % splits || lda % 8 || ldb % 8) return hipErrorInvalidValue;
+  const EpiPartBf16 e{P, N, (size_t)M * N};
+  switch (K / 64 / splits) {
+    case 20: return launch_ws<128, 160, 4, 1, 4, 20, 6>(A, lda, B, ldb, M, N, e, RowMapIdentity{}, s, splits);
+    case 40: return launch_ws<128, 160, 4, 1, 4, 40, 6>(A, lda, B, ldb, M, N, e, RowMapIdentity{}, s, splits);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t gemm_bf16_splitk_any_f32(const void* A, int lda, const void* B, int ldb, int M, int N, int K, int splits,
                                     float* P, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
@@ -1006,12 +1048,12 @@ hipError_t gemm_i8w_act_bf16(const void* A, int lda, const int8_t* B, int ldb, c
 }
 
 
-hipError_t gemm_i8w_splitk_f32(const void* A, int lda, const int8_t* B, int ldb, const float* scale, int M, int N,
-                               int K, int splits, float* P, hipStream_t s) {
+hipError_t gemm_i8w_splitk_bf16(const void* A, int lda, const int8_t* B, int ldb, const float* scale, int M, int N,
+                                int K, int splits, uint16_t* P, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (!i8_shape_ok(A, lda, ldb, N, K, 160) || (splits != 2 && splits != 4) || (K / 64) % splits)
     return hipErrorInvalidValue;
-  const EpiPartF32 e{P, N, (size_t)M * N};
+  const EpiPartBf16 e{P, N, (size_t)M * N};
   switch (K / 64 / splits) {
     case 20: return launch_ws_i8<128, 160, 4, 1, 4, 20>(A, lda, B, ldb, scale, M, N, e, RowMapIdentity{}, s, splits);
     case 10: return launch_ws_i8<128, 160, 4, 1, 4, 10>(A, lda, B, ldb, scale, M, N, e, RowMapIdentity{}, s, splits);

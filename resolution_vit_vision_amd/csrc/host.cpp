@@ -476,7 +476,7 @@ qv_status make_plan(const qv_vision_cfg* c, const int32_t* grid_thw, int32_t n_i
   }
   vp.off_part = o;
   const int max_split = std::max(vp.split_fc2, vp.split_proj);
-  if (max_split > 1) o = align_up(o + (size_t)max_split * N * c->dim * sizeof(float));
+  if (max_split > 1) o = align_up(o + (size_t)max_split * N * c->dim * sizeof(uint16_t));
   if (vp.i8 && c->depth > 0) {
     const int n = (int)N;
     vp.wide_qkv = gemm_i8w_wide(n, 3 * c->dim);
@@ -626,7 +626,7 @@ qv_status vision_forward_impl(const qv_vision_cfg* c, const qv_vision_w* w, cons
   // Split-K (small M): fc2 leaves float32 partial sums; the next block's
   // first LayerNorm adds them, the bias and the residual in a fixed order
   // (after the last block a residual-only pass does it).
-  float* part = reinterpret_cast<float*>(base + vp.off_part);
+  uint16_t* part = reinterpret_cast<uint16_t*>(base + vp.off_part);
   const size_t part_stride = (size_t)vp.N * c->dim;
   int pending = 0;
   const float* pending_bias = nullptr;
@@ -663,7 +663,7 @@ qv_status vision_forward_impl(const qv_vision_cfg* c, const qv_vision_w* w, cons
       else
         QV_LAUNCH(QV_KC_ATTENTION, s, attention_bf16(ab, s));
       if (vp.i8 && vp.split_proj > 1) {
-        QV_LAUNCH(QV_KC_PROJ, s, gemm_i8w_splitk_f32(O, D, (const int8_t*)b.proj_w, D, b.proj_s, M, D, D, vp.split_proj,
+        QV_LAUNCH(QV_KC_PROJ, s, gemm_i8w_splitk_bf16(O, D, (const int8_t*)b.proj_w, D, b.proj_s, M, D, D, vp.split_proj,
                                                      part, s));
         pending = vp.split_proj;
         pending_bias = (const float*)b.proj_b;
@@ -702,7 +702,7 @@ qv_status vision_forward_impl(const qv_vision_cfg* c, const qv_vision_w* w, cons
         QV_LAUNCH(QV_KC_FC2, s, gemm_i8w_wide_resid_f32(H, F, codes, F, b.fc2_s, M, D, F, (const float*)b.fc2_b,
                                                         hidden, D, s));
       } else if (vp.split_fc2 > 1) {
-        QV_LAUNCH(QV_KC_FC2, s, gemm_i8w_splitk_f32(H, F, (const int8_t*)b.fc2_w, F, b.fc2_s, M, D, F, vp.split_fc2,
+        QV_LAUNCH(QV_KC_FC2, s, gemm_i8w_splitk_bf16(H, F, (const int8_t*)b.fc2_w, F, b.fc2_s, M, D, F, vp.split_fc2,
                                                     part, s));
         pending = vp.split_fc2;
         pending_bias = (const float*)b.fc2_b;
@@ -713,7 +713,7 @@ qv_status vision_forward_impl(const qv_vision_cfg* c, const qv_vision_w* w, cons
     } else if (bf) {
       QV_LAUNCH(QV_KC_FC1, s, gemm_bf16_act_bf16(A, D, b.fc1_w, D, M, F, D, (const float*)b.fc1_b, Act::QuickGelu, H, F, s));
       if (vp.split_fc2 > 1) {
-        QV_LAUNCH(QV_KC_FC2, s, gemm_bf16_splitk_f32(H, F, b.fc2_w, F, M, D, F, vp.split_fc2, part, s));
+        QV_LAUNCH(QV_KC_FC2, s, gemm_bf16_splitk_bf16(H, F, b.fc2_w, F, M, D, F, vp.split_fc2, part, s));
         pending = vp.split_fc2;
         pending_bias = (const float*)b.fc2_b;
       } else {

@@ -319,13 +319,19 @@ __global__ __launch_bounds__(256) void k_layernorm(const float* __restrict__ x, 
   }
 }
 
+// Four bf16 values (two packed words) widened to float32 (exact).
+__device__ __forceinline__ float4 bf16x4_to_f32(uint2 w) {
+  return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u), __uint_as_float(w.y << 16),
+                     __uint_as_float(w.y & 0xFFFF0000u));
+}
+
 // Residual update from split-K partial sums, then LayerNorm of the result:
-// x = x + ((p_0 + p_1 + ... + p_{S-1}) + pb), summed in that order, written
-// back; then y = LN(x) as in k_layernorm when g is non-null.  Same one
-// memory round trip: the row, the S partial rows, pb, g and b are loaded up
-// front.
+// x = x + ((p_0 + p_1 + ... + p_{S-1}) + pb), the bf16 partial rows widened
+// and summed in that order in float32, written back; then y = LN(x) as in
+// k_layernorm when g is non-null.  Same one memory round trip: the row, the
+// S partial rows, pb, g and b are loaded up front.
 template <int NV, int S>
-__global__ __launch_bounds__(256) void k_layernorm_acc(float* __restrict__ x, const float* __restrict__ parts,
+__global__ __launch_bounds__(256) void k_layernorm_acc(float* __restrict__ x, const uint16_t* __restrict__ parts,
                                                        size_t part_stride, const float* __restrict__ pb,
                                                        const float* __restrict__ g, const float* __restrict__ b,
                                                        void* __restrict__ y, int bf16, int rows, float eps) {
@@ -338,13 +344,15 @@ __global__ __launch_bounds__(256) void k_layernorm_acc(float* __restrict__ x, co
 #pragma unroll
   for (int i = 0; i < NV; ++i) v[i] = xr[i * 64 + lane];
 #pragma unroll
-  for (int i = 0; i < NV; ++i) acc[i] = reinterpret_cast<const float4*>(parts + (size_t)row * D)[i * 64 + lane];
+  for (int i = 0; i < NV; ++i)
+    acc[i] = bf16x4_to_f32(reinterpret_cast<const uint2*>(parts + (size_t)row * D)[i * 64 + lane]);
   float4 pp[S - 1][NV];
 #pragma unroll
   for (int k = 1; k < S; ++k)
 #pragma unroll
     for (int i = 0; i < NV; ++i)
-      pp[k - 1][i] = reinterpret_cast<const float4*>(parts + k * part_stride + (size_t)row * D)[i * 64 + lane];
+      pp[k - 1][i] =
+          bf16x4_to_f32(reinterpret_cast<const uint2*>(parts + k * part_stride + (size_t)row * D)[i * 64 + lane]);
 #pragma unroll
   for (int i = 0; i < NV; ++i) bias[i] = reinterpret_cast<const float4*>(pb)[i * 64 + lane];
   float4 gg[NV], bb[NV];
@@ -447,7 +455,7 @@ __global__ __launch_bounds__(320) void k_layernorm_r5(const float* __restrict__ 
 }
 
 template <int S>
-__global__ __launch_bounds__(320) void k_layernorm_acc_r5(float* __restrict__ x, const float* __restrict__ parts,
+__global__ __launch_bounds__(320) void k_layernorm_acc_r5(float* __restrict__ x, const uint16_t* __restrict__ parts,
                                                           size_t part_stride, const float* __restrict__ pb,
                                                           const float* __restrict__ g, const float* __restrict__ b,
                                                           void* __restrict__ y, int bf16, float eps) {
@@ -457,7 +465,8 @@ __global__ __launch_bounds__(320) void k_layernorm_acc_r5(float* __restrict__ x,
   float4 v = xr[tid];
   float4 p[S];
 #pragma unroll
-  for (int k = 0; k < S; ++k) p[k] = reinterpret_cast<const float4*>(parts + k * part_stride + (size_t)row * 1280)[tid];
+  for (int k = 0; k < S; ++k)
+    p[k] = bf16x4_to_f32(reinterpret_cast<const uint2*>(parts + k * part_stride + (size_t)row * 1280)[tid]);
   const float4 bias = reinterpret_cast<const float4*>(pb)[tid];
   float4 gg = make_float4(0.f, 0.f, 0.f, 0.f), bb = gg;
   if (g) {
@@ -475,7 +484,7 @@ __global__ __launch_bounds__(320) void k_layernorm_acc_r5(float* __restrict__ x,
   row5_norm_store(v, gg, bb, y, bf16, row, tid, eps, red, wave, lane);
 }
 
-hipError_t launch_layernorm_acc(float* x, const float* parts, size_t part_stride, int splits, const float* pb,
+hipError_t launch_layernorm_acc(float* x, const uint16_t* parts, size_t part_stride, int splits, const float* pb,
                                 const float* g, const float* b, void* y, bool bf16, int rows, int dim, float eps,
                                 hipStream_t s) {
   if (dim != 1280) return hipErrorInvalidValue;

@@ -142,8 +142,8 @@ hipError_t gemm_i8w_qkv(const void* A, int lda, const int8_t* B, int ldb, const 
 hipError_t gemm_i8w_act_bf16(const void* A, int lda, const int8_t* B, int ldb, const float* scale, int M, int N,
                              int K, const float* bias, Act act, void* C, int ldc, hipStream_t s);
 int gemm_i8w_runs(int M, int N, int K);
-hipError_t gemm_i8w_splitk_f32(const void* A, int lda, const int8_t* B, int ldb, const float* scale, int M, int N,
-                               int K, int splits, float* P, hipStream_t s);
+hipError_t gemm_i8w_splitk_bf16(const void* A, int lda, const int8_t* B, int ldb, const float* scale, int M, int N,
+                                int K, int splits, uint16_t* P, hipStream_t s);
 hipError_t gemm_i8w_resid_f32(const void* A, int lda, const int8_t* B, int ldb, const float* scale, int M, int N,
                               int K, const float* bias, float* Z, int ldz, hipStream_t s);
 hipError_t launch_quantize_i8(const void* w, int rows, int cols, int ld, bool bf16, int8_t* q, float* scale,
@@ -171,8 +171,12 @@ hipError_t launch_splitk_reduce(const float* P, int splits, size_t stride, const
 // P[s][M][N] = A[:, s K/S .. (s+1) K/S) . B[:, same]^T, float32, no bias.
 hipError_t gemm_bf16_splitk_f32(const void* A, int lda, const void* B, int ldb, int M, int N, int K, int splits,
                                 float* P, hipStream_t s);
-// x += sum_s parts[s] + pb (in that order); y = LN(x) if g is non-null.
-hipError_t launch_layernorm_acc(float* x, const float* parts, size_t part_stride, int splits, const float* pb,
+// The same with each run's sums rounded to bf16 (the tower's fc2).
+hipError_t gemm_bf16_splitk_bf16(const void* A, int lda, const void* B, int ldb, int M, int N, int K, int splits,
+                                 uint16_t* P, hipStream_t s);
+// x += sum_s parts[s] + pb (bf16 partial rows widened to float32, added in
+// that order); y = LN(x) if g is non-null.
+hipError_t launch_layernorm_acc(float* x, const uint16_t* parts, size_t part_stride, int splits, const float* pb,
                                 const float* g, const float* b, void* y, bool bf16, int rows, int dim, float eps,
                                 hipStream_t s);
 hipError_t gemm_bf16_act_bf16(const void* A, int lda, const void* B, int ldb, int M, int N, int K,

@@ -46,7 +46,7 @@ def _pair(images, depth, window=0, full_blocks=(), weights="dtype"):
 
 def test_noalloc_matches_workspace_forward_twice():
     import resolution_vit_vision_amd as qv
-    # first call: one 448x448 image, 4 blocks (42.5 MiB of workspace at full depth)
+    # first call: one 448x448 image, 4 blocks (32.5 MiB of workspace at full depth)
     _say("no-alloc call 1: 448x448, 4 blocks")
     enc, ref, got = _pair([(448, 448, 1)], depth=4)
     from resolution_vit_vision_amd import _abi
