@@ -113,6 +113,8 @@ SMALL = [
     ("ragged3_fp32", [(84, 140, 1), (56, 56, 1), (224, 252, 1)], 1, "f32"),
     ("ragged3_bf16", [(84, 140, 1), (56, 56, 1), (224, 252, 1)], 2, "bf16"),
     ("tiles_bf16", [(252, 364, 1), (112, 56, 1)], 2, "bf16"),
+    # M = 1088: fc2 splits K in two runs (bf16 partial sums), ragged last row tile
+    ("pair1088_bf16", [(448, 448, 1), (112, 112, 1)], 2, "bf16"),
     ("video_bf16", [(84, 112, 3)], 1, "bf16"),
 ]
 
