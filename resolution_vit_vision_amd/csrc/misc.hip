@@ -443,22 +443,55 @@ __device__ __forceinline__ void row5_norm_store(float4 v, float4 gg, float4 bb, 
   }
 }
 
+// Cache warming beside a few-row LayerNorm: the workgroups read n16 16-byte
+// chunks of p grid-stride, issued after the row's own loads (so waiting for
+// those, in order, never waits for these) and folded into one word that is
+// stored only through a null pointer check the host never passes (sink is
+// always null), which keeps the loads without writing anything.
+struct WarmArgs {
+  const uint4* p;
+  size_t n16;
+  uint32_t* sink;
+};
+__device__ __forceinline__ uint32_t warm_issue(const WarmArgs& w, int tid) {
+  uint32_t acc = 0;
+  const size_t stride = (size_t)gridDim.x * 320;
+  // four loads in flight per round (a matrix of up to 4 x 16 B per thread of
+  // the grid takes one round)
+  for (size_t i0 = (size_t)blockIdx.x * 320 + tid; i0 < w.n16; i0 += 4 * stride) {
+    uint4 v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const size_t i = i0 + k * stride;
+      v[k] = i < w.n16 ? w.p[i] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+  }
+  return acc;
+}
+__device__ __forceinline__ void warm_retire(const WarmArgs& w, uint32_t acc) {
+  if (w.sink && acc == 0x9E3779B9u) *w.sink = acc;
+}
+
 __global__ __launch_bounds__(320) void k_layernorm_r5(const float* __restrict__ x, const float* __restrict__ g,
                                                       const float* __restrict__ b, void* __restrict__ y, int bf16,
-                                                      float eps) {
+                                                      float eps, WarmArgs warm) {
   __shared__ float red[16];
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float4 v = reinterpret_cast<const float4*>(x + (size_t)row * 1280)[tid];
   const float4 gg = reinterpret_cast<const float4*>(g)[tid];
   const float4 bb = reinterpret_cast<const float4*>(b)[tid];
+  const uint32_t wacc = warm_issue(warm, tid);
   row5_norm_store(v, gg, bb, y, bf16, row, tid, eps, red, wave, lane);
+  warm_retire(warm, wacc);
 }
 
 template <int S>
 __global__ __launch_bounds__(320) void k_layernorm_acc_r5(float* __restrict__ x, const uint16_t* __restrict__ parts,
                                                           size_t part_stride, const float* __restrict__ pb,
                                                           const float* __restrict__ g, const float* __restrict__ b,
-                                                          void* __restrict__ y, int bf16, float eps) {
+                                                          void* __restrict__ y, int bf16, float eps, WarmArgs warm) {
   __shared__ float red[16];
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   float4* xr = reinterpret_cast<float4*>(x + (size_t)row * 1280);
@@ -473,6 +506,7 @@ __global__ __launch_bounds__(320) void k_layernorm_acc_r5(float* __restrict__ x,
     gg = reinterpret_cast<const float4*>(g)[tid];
     bb = reinterpret_cast<const float4*>(b)[tid];
   }
+  const uint32_t wacc = warm_issue(warm, tid);
   float4 acc = p[0];
 #pragma unroll
   for (int k = 1; k < S; ++k) {
@@ -480,22 +514,23 @@ __global__ __launch_bounds__(320) void k_layernorm_acc_r5(float* __restrict__ x,
   }
   v.x += acc.x + bias.x; v.y += acc.y + bias.y; v.z += acc.z + bias.z; v.w += acc.w + bias.w;
   xr[tid] = v;
-  if (!g) return;  // uniform over the workgroup
-  row5_norm_store(v, gg, bb, y, bf16, row, tid, eps, red, wave, lane);
+  if (g) row5_norm_store(v, gg, bb, y, bf16, row, tid, eps, red, wave, lane);  // uniform over the workgroup
+  warm_retire(warm, wacc);
 }
 
 hipError_t launch_layernorm_acc(float* x, const uint16_t* parts, size_t part_stride, int splits, const float* pb,
                                 const float* g, const float* b, void* y, bool bf16, int rows, int dim, float eps,
-                                hipStream_t s) {
+                                hipStream_t s, CacheWarm warm) {
   if (dim != 1280) return hipErrorInvalidValue;
   if (rows <= 0) return hipSuccess;
   if (rows <= kLnFewRows) {
     const dim3 grid((unsigned)rows);
+    const WarmArgs wa{reinterpret_cast<const uint4*>(warm.p), warm.p ? warm.bytes / 16 : 0, nullptr};
     switch (splits) {
       case 2: QV_KLAUNCH((k_layernorm_acc_r5<2>), grid, dim3(320), 0, s, x, parts, part_stride, pb, g, b, y,
-                         bf16 ? 1 : 0, eps); break;
+                         bf16 ? 1 : 0, eps, wa); break;
       case 4: QV_KLAUNCH((k_layernorm_acc_r5<4>), grid, dim3(320), 0, s, x, parts, part_stride, pb, g, b, y,
-                         bf16 ? 1 : 0, eps); break;
+                         bf16 ? 1 : 0, eps, wa); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -512,10 +547,11 @@ hipError_t launch_layernorm_acc(float* x, const uint16_t* parts, size_t part_str
 }
 
 hipError_t launch_layernorm(const float* x, const float* g, const float* b, void* y, bool bf16, int rows, int dim,
-                            float eps, hipStream_t s) {
+                            float eps, hipStream_t s, CacheWarm warm) {
   if (rows <= 0) return hipSuccess;
   if (dim == 1280 && rows <= kLnFewRows) {
-    QV_KLAUNCH(k_layernorm_r5, dim3((unsigned)rows), dim3(320), 0, s, x, g, b, y, bf16 ? 1 : 0, eps);
+    const WarmArgs wa{reinterpret_cast<const uint4*>(warm.p), warm.p ? warm.bytes / 16 : 0, nullptr};
+    QV_KLAUNCH(k_layernorm_r5, dim3((unsigned)rows), dim3(320), 0, s, x, g, b, y, bf16 ? 1 : 0, eps, wa);
     return hipGetLastError();
   }
   dim3 grid((unsigned)((rows + 3) / 4));

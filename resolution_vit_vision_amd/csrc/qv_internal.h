@@ -109,8 +109,15 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 // on the current device (looked up once per device, then cached).
 hipError_t scratch_buffer(void** ptr);
 
+// Bytes a LayerNorm of few rows reads beside its rows, to bring the weight
+// matrix of a later product into the Infinity Cache before that product
+// runs (nothing is written; null / 0: none).
+struct CacheWarm {
+  const void* p = nullptr;
+  size_t bytes = 0;
+};
 hipError_t launch_layernorm(const float* x, const float* g, const float* b, void* y, bool bf16, int rows,
-                            int dim, float eps, hipStream_t s);
+                            int dim, float eps, hipStream_t s, CacheWarm warm = {});
 
 // K of the bf16 path is stored key-tiled and chunk-major per head:
 // [head][P / 32][10 chunks of 8 dims][32 keys][8 dims], so the 32 key rows an
@@ -178,7 +185,7 @@ hipError_t gemm_bf16_splitk_bf16(const void* A, int lda, const void* B, int ldb,
 // that order); y = LN(x) if g is non-null.
 hipError_t launch_layernorm_acc(float* x, const uint16_t* parts, size_t part_stride, int splits, const float* pb,
                                 const float* g, const float* b, void* y, bool bf16, int rows, int dim, float eps,
-                                hipStream_t s);
+                                hipStream_t s, CacheWarm warm = {});
 hipError_t gemm_bf16_act_bf16(const void* A, int lda, const void* B, int ldb, int M, int N, int K,
                               const float* bias, Act act, void* C, int ldc, hipStream_t s);
 hipError_t gemm_bf16_qkv(const void* A, int lda, const void* B, int ldb, int M, int K, const float* bias,

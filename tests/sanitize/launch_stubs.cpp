@@ -22,7 +22,7 @@ hipError_t launch_setup_plan(const PlanEntry* host_plan_chunk, int count, int fi
 }
 hipError_t launch_rope_table(float2* tab, int positions, float theta, hipStream_t s) { return hipSuccess; }
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) { return hipSuccess; }
-hipError_t launch_layernorm(const float* x, const float* g, const float* b, void* y, bool bf16, int rows, int dim, float eps, hipStream_t s) { return hipSuccess; }
+hipError_t launch_layernorm(const float* x, const float* g, const float* b, void* y, bool bf16, int rows, int dim, float eps, hipStream_t s, CacheWarm warm) { return hipSuccess; }
 hipError_t gemm_bf16_store_f32(const void* A, int lda, const void* B, int ldb, int M, int N, int K, const float* bias, float* C, int ldc, hipStream_t s) { return hipSuccess; }
 hipError_t gemm_bf16_resid_f32(const void* A, int lda, const void* B, int ldb, int M, int N, int K, const float* bias, float* Z, int ldz, hipStream_t s) { return hipSuccess; }
 hipError_t gemm_i8w_qkv(const void* A, int lda, const int8_t* B, int ldb, const float* scale, int M, int K, const float* bias, const QkvOut& o, hipStream_t s) { return hipSuccess; }
@@ -38,7 +38,7 @@ hipError_t gemm_bf16_splitk_any_f32(const void* A, int lda, const void* B, int l
 hipError_t launch_splitk_reduce(const float* P, int splits, size_t stride, const float* bias, Act act, void* out, int ldo, int M, int N, hipStream_t s) { return hipSuccess; }
 hipError_t gemm_bf16_splitk_f32(const void* A, int lda, const void* B, int ldb, int M, int N, int K, int splits, float* P, hipStream_t s) { return hipSuccess; }
 hipError_t gemm_bf16_splitk_bf16(const void* A, int lda, const void* B, int ldb, int M, int N, int K, int splits, uint16_t* P, hipStream_t s) { return hipSuccess; }
-hipError_t launch_layernorm_acc(float* x, const uint16_t* parts, size_t part_stride, int splits, const float* pb, const float* g, const float* b, void* y, bool bf16, int rows, int dim, float eps, hipStream_t s) { return hipSuccess; }
+hipError_t launch_layernorm_acc(float* x, const uint16_t* parts, size_t part_stride, int splits, const float* pb, const float* g, const float* b, void* y, bool bf16, int rows, int dim, float eps, hipStream_t s, CacheWarm warm) { return hipSuccess; }
 hipError_t gemm_bf16_act_bf16(const void* A, int lda, const void* B, int ldb, int M, int N, int K, const float* bias, Act act, void* C, int ldc, hipStream_t s) { return hipSuccess; }
 hipError_t gemm_bf16_qkv(const void* A, int lda, const void* B, int ldb, int M, int K, const float* bias, const QkvOut& o, hipStream_t s) { return hipSuccess; }
 hipError_t gemm_f32_store(const float* A, int lda, const float* B, int ldb, int M, int N, int K, const float* bias, float* C, int ldc, hipStream_t s) { return hipSuccess; }
