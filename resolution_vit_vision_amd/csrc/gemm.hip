@@ -770,17 +770,18 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(const uint16_t* __restrict__ 
   epi.apply(acc, m0 + wm * TM, n0 + wn * TN, lane, M, N);
 }
 
-// XCD cut of the tile grid (see tile_coords): the xgn in {1, 2, 4, 8} whose
-// rectangles need the fewest A + B rows per XCD, and the grid size.
+// XCD cut of the tile grid over nx XCD groups (see tile_coords_in): the xgn
+// in {1, 2, .., nx} whose rectangles need the fewest A + B rows per XCD, and
+// the grid size (8 x the largest rectangle).
 struct XcdCut {
   int xgn;
   unsigned grid;
 };
-static XcdCut xcd_cut(int tiles_m, int tiles_n, int BM, int BN) {
+static XcdCut xcd_cut(int tiles_m, int tiles_n, int BM, int BN, int nx = 8) {
   XcdCut best{1, 0};
   int64_t best_rows = -1;
-  for (int xgn = 1; xgn <= 8; xgn *= 2) {
-    const int xgm = 8 / xgn;
+  for (int xgn = 1; xgn <= nx; xgn *= 2) {
+    const int xgm = nx / xgn;
     const int64_t rm = (tiles_m + xgm - 1) / xgm, rn = (tiles_n + xgn - 1) / xgn;
     const int64_t rows = rm * BM + rn * BN;
     if (best_rows < 0 || rows < best_rows) {
@@ -806,12 +807,15 @@ static hipError_t launch_pipe(const void* A, int lda, const void* B, int ldb, in
 template <int BM, int BN, int WM, int WN, int ST, int KT, int NP, class Epi, class RowMap>
 static hipError_t launch_ws(const void* A, int lda, const void* B, int ldb, int M, int N, const Epi& epi,
                             RowMap rmap, hipStream_t s, int splits = 1) {
-  const XcdCut cut = xcd_cut((M + BM - 1) / BM, (N + BN - 1) / BN, BM, BN);
-  // the grid width is a multiple of 8, so workgroup (x, y) still runs on XCD x % 8
-  QV_KLAUNCH((k_gemm_ws<BM, BN, WM, WN, ST, KT, NP, Epi, RowMap>), dim3(cut.grid, (unsigned)splits),
+  // runs that divide the 8 XCDs get XCDs of their own (one grid row);
+  // otherwise the grid width is a multiple of 8, so workgroup (x, y) still
+  // runs on XCD x % 8 and y is the run
+  const bool xruns = splits > 1 && 8 % splits == 0;
+  const XcdCut cut = xcd_cut((M + BM - 1) / BM, (N + BN - 1) / BN, BM, BN, xruns ? 8 / splits : 8);
+  QV_KLAUNCH((k_gemm_ws<BM, BN, WM, WN, ST, KT, NP, Epi, RowMap>), dim3(cut.grid, xruns ? 1u : (unsigned)splits),
                      dim3((WM * WN + NP) * 64), 0,
                      s, reinterpret_cast<const uint16_t*>(A), lda, reinterpret_cast<const uint16_t*>(B), ldb, M, N,
-                     cut.xgn, 8, epi, rmap);
+                     cut.xgn, 8, xruns ? splits : 1, epi, rmap);
   return hipGetLastError();
 }
 

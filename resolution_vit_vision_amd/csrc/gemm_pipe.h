@@ -175,10 +175,11 @@ __device__ __forceinline__ void pipe_compute(const uint16_t* stage, f32x16 (&acc
 // flight are shared by concurrent workgroups.  Rectangles differ by at most
 // one row / column tile; the grid has 8 x (largest rectangle) workgroups and
 // the surplus ones of smaller rectangles return at once (valid = false).
-__device__ __forceinline__ bool tile_coords(int bid, int tiles_m, int tiles_n, int xgn, int group, int& tm,
-                                            int& tn) {
-  const int xgm = 8 / xgn;
-  const int x = bid % 8, i = bid / 8;
+// tile_coords_in cuts the grid over nx XCD groups (xgm * xgn = nx) and
+// returns tile i of group x's rectangle.
+__device__ __forceinline__ bool tile_coords_in(int x, int i, int nx, int tiles_m, int tiles_n, int xgn, int group,
+                                               int& tm, int& tn) {
+  const int xgm = nx / xgn;
   const int gx = x / xgn, gy = x % xgn;
   const int tm0 = gx * tiles_m / xgm, tm1 = (gx + 1) * tiles_m / xgm;
   const int tn0 = gy * tiles_n / xgn, tn1 = (gy + 1) * tiles_n / xgn;
@@ -191,6 +192,11 @@ __device__ __forceinline__ bool tile_coords(int bid, int tiles_m, int tiles_n, i
   tm = tm0 + first + r % gsz;
   tn = tn0 + r / gsz;
   return true;
+}
+
+__device__ __forceinline__ bool tile_coords(int bid, int tiles_m, int tiles_n, int xgn, int group, int& tm,
+                                            int& tn) {
+  return tile_coords_in(bid % 8, bid / 8, 8, tiles_m, tiles_n, xgn, group, tm, tn);
 }
 
 // Statically unrolled K loop: with no loop-carried merge point the compiler
@@ -349,10 +355,15 @@ struct WsConsumer {
   }
 };
 
-// Split-K: workgroup row blockIdx.y multiplies the y-th run of KT * 64
-// columns of A and B, and its epilogue is the one epi_at_split() derives for
-// that run (a partial-sum epilogue writes its own slice; every other
-// epilogue is used as is, with one run).
+// Split-K: a workgroup multiplies the r-th run of KT * 64 columns of A and B,
+// and its epilogue is the one epi_at_split() derives for that run (a
+// partial-sum epilogue writes its own slice; every other epilogue is used as
+// is, with one run).  With xruns = 1 the run is blockIdx.y and every XCD
+// takes a rectangle of every run's tiles.  With xruns in {2, 4, 8} the grid
+// is one row and the runs are spread over the XCDs instead: XCD x works on
+// run x / (8 / xruns) only, and the 8 / xruns XCDs of a run cut its tile
+// grid into rectangles, so an XCD fetches the A and B panels of one K range
+// (fewer, larger rectangles share more of each panel).
 template <class E>
 __device__ __forceinline__ E epi_at_split(const E& e, int) {
   return e;
@@ -361,7 +372,8 @@ __device__ __forceinline__ E epi_at_split(const E& e, int) {
 template <int BM, int BN, int WM, int WN, int STAGES, int KT, int NP, class Epi, class RowMap>
 __global__ __launch_bounds__((WM * WN + NP) * 64) void k_gemm_ws(const uint16_t* __restrict__ A, int lda,
                                                                 const uint16_t* __restrict__ B, int ldb, int M,
-                                                                int N, int xgn, int group, Epi epi_all, RowMap rmap) {
+                                                                int N, int xgn, int group, int xruns, Epi epi_all,
+                                                                RowMap rmap) {
   using C = PipeCfg<BM, BN, WM, WN, STAGES>;
   constexpr int NC = WM * WN;
   constexpr int BLOCKS = (BM + BN) * 8 / 64;  // 1 KB blocks per stage
@@ -382,12 +394,19 @@ __global__ __launch_bounds__((WM * WN + NP) * 64) void k_gemm_ws(const uint16_t*
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tiles_n = (N + BN - 1) / BN, tiles_m = (M + BM - 1) / BM;
-  int tm, tn;
-  if (!tile_coords(blockIdx.x, tiles_m, tiles_n, xgn, group, tm, tn)) return;  // uniform over the workgroup
+  int tm, tn, run;
+  if (xruns > 1) {
+    const int x = blockIdx.x % 8, nx = 8 / xruns;
+    run = x / nx;
+    if (!tile_coords_in(x % nx, blockIdx.x / 8, nx, tiles_m, tiles_n, xgn, group, tm, tn)) return;
+  } else {
+    run = blockIdx.y;
+    if (!tile_coords(blockIdx.x, tiles_m, tiles_n, xgn, group, tm, tn)) return;  // uniform over the workgroup
+  }
   const int m0 = tm * BM, n0 = tn * BN;
-  A += (size_t)blockIdx.y * KT * 64;
-  B += (size_t)blockIdx.y * KT * 64;
-  const Epi epi = epi_at_split(epi_all, (int)blockIdx.y);
+  A += (size_t)run * KT * 64;
+  B += (size_t)run * KT * 64;
+  const Epi epi = epi_at_split(epi_all, run);
 
   if (wave >= NC) {
     const char* gsrc[LP];
