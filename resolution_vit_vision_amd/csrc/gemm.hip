@@ -1023,10 +1023,13 @@ template <int BM, int BN, int WM, int WN, int ST, int KT, class Epi, class RowMa
 static hipError_t launch_ws_i8(const void* A, int lda, const int8_t* B, int ldb, const float* scale, int M, int N,
                                const Epi& epi, RowMap rmap, hipStream_t s, int splits = 1) {
   constexpr int NPA = 2, NPB = 2;
-  const XcdCut cut = xcd_cut((M + BM - 1) / BM, (N + BN - 1) / BN, BM, BN);
-  QV_KLAUNCH((k_gemm_ws_i8<BM, BN, WM, WN, ST, KT, NPA, NPB, Epi, RowMap>), dim3(cut.grid, (unsigned)splits),
-             dim3((WM * WN + NPA + NPB) * 64), 0, s, reinterpret_cast<const uint16_t*>(A), lda, B, ldb, scale, M, N,
-             cut.xgn, 8, epi, rmap);
+  // K runs spread over the XCDs as in launch_ws
+  const bool xruns = splits > 1 && 8 % splits == 0;
+  const XcdCut cut = xcd_cut((M + BM - 1) / BM, (N + BN - 1) / BN, BM, BN, xruns ? 8 / splits : 8);
+  QV_KLAUNCH((k_gemm_ws_i8<BM, BN, WM, WN, ST, KT, NPA, NPB, Epi, RowMap>),
+             dim3(cut.grid, xruns ? 1u : (unsigned)splits), dim3((WM * WN + NPA + NPB) * 64), 0, s,
+             reinterpret_cast<const uint16_t*>(A), lda, B, ldb, scale, M, N, cut.xgn, 8, xruns ? splits : 1, epi,
+             rmap);
   return hipGetLastError();
 }
 

@@ -369,6 +369,17 @@ __device__ __forceinline__ E epi_at_split(const E& e, int) {
   return e;
 }
 
+__device__ __forceinline__ bool run_tile_coords(int xruns, int tiles_m, int tiles_n, int xgn, int group, int& tm,
+                                                int& tn, int& run) {
+  if (xruns > 1) {
+    const int x = blockIdx.x % 8, nx = 8 / xruns;
+    run = x / nx;
+    return tile_coords_in(x % nx, blockIdx.x / 8, nx, tiles_m, tiles_n, xgn, group, tm, tn);
+  }
+  run = blockIdx.y;
+  return tile_coords(blockIdx.x, tiles_m, tiles_n, xgn, group, tm, tn);
+}
+
 template <int BM, int BN, int WM, int WN, int STAGES, int KT, int NP, class Epi, class RowMap>
 __global__ __launch_bounds__((WM * WN + NP) * 64) void k_gemm_ws(const uint16_t* __restrict__ A, int lda,
                                                                 const uint16_t* __restrict__ B, int ldb, int M,
@@ -395,14 +406,7 @@ __global__ __launch_bounds__((WM * WN + NP) * 64) void k_gemm_ws(const uint16_t*
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tiles_n = (N + BN - 1) / BN, tiles_m = (M + BM - 1) / BM;
   int tm, tn, run;
-  if (xruns > 1) {
-    const int x = blockIdx.x % 8, nx = 8 / xruns;
-    run = x / nx;
-    if (!tile_coords_in(x % nx, blockIdx.x / 8, nx, tiles_m, tiles_n, xgn, group, tm, tn)) return;
-  } else {
-    run = blockIdx.y;
-    if (!tile_coords(blockIdx.x, tiles_m, tiles_n, xgn, group, tm, tn)) return;  // uniform over the workgroup
-  }
+  if (!run_tile_coords(xruns, tiles_m, tiles_n, xgn, group, tm, tn, run)) return;  // uniform over the workgroup
   const int m0 = tm * BM, n0 = tn * BN;
   A += (size_t)run * KT * 64;
   B += (size_t)run * KT * 64;
@@ -572,7 +576,7 @@ struct I8BProd {
 template <int BM, int BN, int WM, int WN, int STAGES, int KT, int NPA, int NPB, class Epi, class RowMap>
 __global__ __launch_bounds__((WM * WN + NPA + NPB) * 64) void k_gemm_ws_i8(
     const uint16_t* __restrict__ A, int lda, const int8_t* __restrict__ B, int ldb, const float* __restrict__ bscale,
-    int M, int N, int xgn, int group, Epi epi_all, RowMap rmap) {
+    int M, int N, int xgn, int group, int xruns, Epi epi_all, RowMap rmap) {
   using C = PipeCfg<BM, BN, WM, WN, STAGES>;
   constexpr int NC = WM * WN;
   constexpr int ABLK = BM * 8 / 64;
@@ -590,12 +594,12 @@ __global__ __launch_bounds__((WM * WN + NPA + NPB) * 64) void k_gemm_ws_i8(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tiles_n = (N + BN - 1) / BN, tiles_m = (M + BM - 1) / BM;
-  int tm, tn;
-  if (!tile_coords(blockIdx.x, tiles_m, tiles_n, xgn, group, tm, tn)) return;  // uniform over the workgroup
+  int tm, tn, run;
+  if (!run_tile_coords(xruns, tiles_m, tiles_n, xgn, group, tm, tn, run)) return;  // uniform over the workgroup
   const int m0 = tm * BM, n0 = tn * BN;
-  A += (size_t)blockIdx.y * KT * 64;
-  B += (size_t)blockIdx.y * KT * 64;
-  const Epi epi = epi_at_split(epi_all, (int)blockIdx.y);
+  A += (size_t)run * KT * 64;
+  B += (size_t)run * KT * 64;
+  const Epi epi = epi_at_split(epi_all, run);
 
   if (wave >= NC + NPA) {
     I8BProd<BM, BN, NPB, STAGES, KT, RowMap> p;
